@@ -1,0 +1,164 @@
+"""CPU oracle for the block-float quantized GEMV / MoE GEMV / prefill GEMM.
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It is a plain C
+library (``oracle.c``, built with gcc -O2, OpenMP over output rows, no
+-ffast-math) behind numpy-facing ctypes wrappers.  It shares no code with the
+HIP library.
+
+Every function returns fp64 results; the GEMV-style ones also return
+``abs_y = sum_k |w*x|`` so a test can apply the acceptance bound
+``|y_gpu - y| <= 1e-5 * abs_y + 1e-6``.
+
+Pins (tests/test_oracle_*.py): E2M1 value table, E8M0 closed form and
+``torch.float8_e8m0fnu``, E4M3 against ``torch.float8_e4m3fn``, the
+scale-bump invariant, exact rational brute force on 4x32 inputs (dense, MoE and
+GEMM rows), one-hot activations and closed-form sums.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MXFP4, MXFP8, NVFP4 = 1, 2, 3
+BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so (always recompiles)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        for name in ("orc_e2m1", "orc_e8m0", "orc_e4m3"):
+            getattr(lib, name).restype = ctypes.c_double
+            getattr(lib, name).argtypes = [ctypes.c_uint]
+        lib.orc_bf16.restype = ctypes.c_double
+        lib.orc_bf16.argtypes = [ctypes.c_uint16]
+        lib.orc_num_threads.restype = I
+        lib.orc_set_num_threads.argtypes = [I]
+        lib.orc_dequant.argtypes = [I, P, P, P, I64, I64, P]
+        lib.orc_gemv.argtypes = [I, P, P, P, P, I64, I64, I64, P, P]
+        lib.orc_moe_gemv.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, I64, I64, P, P]
+        lib.orc_gemm_rows.argtypes = [I, P, P, P, P, P, I64, I64, I64, P, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(fmt, k):
+    if fmt not in BLOCK:
+        raise ValueError(f"unknown format {fmt}")
+    if k % BLOCK[fmt]:
+        raise ValueError(f"k={k} is not a multiple of the block size {BLOCK[fmt]}")
+
+
+def e2m1(c: int) -> float:
+    return _load().orc_e2m1(c)
+
+
+def e8m0(u: int) -> float:
+    return _load().orc_e8m0(u)
+
+
+def e4m3(b: int) -> float:
+    return _load().orc_e4m3(b)
+
+
+def bf16(h: int) -> float:
+    return _load().orc_bf16(h)
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    _load().orc_set_num_threads(n)
+
+
+def dequant(fmt, codes, scales, g, rows, k):
+    """fp32 [rows][k] decoded weights."""
+    _check(fmt, k)
+    codes, scales, g = _c(codes, np.uint8), _c(scales, np.uint8), _c(g, np.float32)
+    w = np.empty((rows, k), dtype=np.float32)
+    _load().orc_dequant(fmt, _ptr(codes), _ptr(scales), _ptr(g), rows, k, _ptr(w))
+    return w
+
+
+def gemv(fmt, codes, scales, g, x, n, k):
+    """(y, abs_y), both fp64 [batch][n]; x is bf16 bits uint16 [batch][k]."""
+    _check(fmt, k)
+    codes, scales, g = _c(codes, np.uint8), _c(scales, np.uint8), _c(g, np.float32)
+    x = _c(x, np.uint16).reshape(-1, k)
+    batch = x.shape[0]
+    y = np.empty((batch, n), dtype=np.float64)
+    a = np.empty((batch, n), dtype=np.float64)
+    _load().orc_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(g), _ptr(x), batch, n, k, _ptr(y), _ptr(a))
+    return y, a
+
+
+def moe_gemv(fmt, codes, scales, g, ids, x, x_per_slot, experts, n, k):
+    """(y, abs_y), both fp64 [tokens][topk][n]."""
+    _check(fmt, k)
+    codes, scales, g = _c(codes, np.uint8), _c(scales, np.uint8), _c(g, np.float32)
+    ids = _c(ids, np.int32)
+    tokens, topk = ids.shape
+    x = _c(x, np.uint16)
+    y = np.empty((tokens, topk, n), dtype=np.float64)
+    a = np.empty((tokens, topk, n), dtype=np.float64)
+    _load().orc_moe_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(g), _ptr(ids), _ptr(x), int(x_per_slot),
+                         experts, n, k, tokens, topk, _ptr(y), _ptr(a))
+    return y, a
+
+
+def gemm_rows(fmt, codes, scales, g, X, rows, n, k):
+    """(Y, abs_Y), both fp64 [len(rows)][n], for the listed token rows of X [m][k]."""
+    _check(fmt, k)
+    codes, scales, g = _c(codes, np.uint8), _c(scales, np.uint8), _c(g, np.float32)
+    X = _c(X, np.uint16)
+    rows = _c(rows, np.int64)
+    Y = np.empty((rows.size, n), dtype=np.float64)
+    A = np.empty((rows.size, n), dtype=np.float64)
+    _load().orc_gemm_rows(fmt, _ptr(codes), _ptr(scales), _ptr(g), _ptr(X), _ptr(rows), rows.size, n, k,
+                          _ptr(Y), _ptr(A))
+    return Y, A
+
+
+def within_tolerance(y_gpu, y_ref, abs_ref, rel=1e-5, atol=1e-6):
+    """Boolean array: |y_gpu - y_ref| <= rel * abs_ref + atol (NaN matches NaN, equal infinities match)."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    both_nan = np.isnan(y_gpu) & np.isnan(y_ref)
+    with np.errstate(invalid="ignore"):
+        ok = np.abs(y_gpu - y_ref) <= rel * abs_ref + atol
+    return ok | both_nan | (y_gpu == y_ref)

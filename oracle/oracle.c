@@ -1,0 +1,217 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the block-float
+ * quantized GEMV, expert-indexed MoE GEMV and prefill GEMM.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this library.  It shares no source, header, table or
+ * helper with the HIP library and the HIP library never calls it.
+ *
+ * What it follows:
+ *  - "MLxcel 0.8 release" post (backend.ai), section "Decoding block-float
+ *    formats in software": MXFP4, MXFP8 and NVFP4 weights are block-float
+ *    formats whose blocks share one scale; they are decoded to ordinary floats
+ *    and then multiplied with the activations.  The same section fixes E2M1 as
+ *    1 sign, 2 exponent and 1 mantissa bit and states that the decode is exact.
+ *  - The same talk as a slide deck ("High-performance LLM/VLM inference on AMD
+ *    Strix Halo with mlxcel engine"), slide 7 (block-float weights are unpacked
+ *    in the kernel, then contracted with FMA) and slide 12 (exact decode).
+ *  - Everything the pages leave open is taken from the public OCP Microscaling
+ *    (MX) v1.0 and NVFP4 definitions:
+ *      MXFP4 = 32 E2M1 codes sharing one E8M0 scale,
+ *      MXFP8 = 32 E4M3 (OCP "FN": bias 7, no infinities) codes + one E8M0 scale,
+ *      NVFP4 = 16 E2M1 codes sharing one E4M3 scale, plus one fp32 scale per
+ *              tensor.
+ *    E8M0 byte u means 2^(u-127); u = 255 is NaN.
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *  - layout: weights W[n][k] row-major; two E2M1 codes per byte with the even k
+ *    in bits 3:0 and the odd k in bits 7:4; MXFP8 one byte per code; block
+ *    scales row-major [n][k/block]; an MoE bank is expert-major [E][n][...].
+ *  - element value: MX w = fl32(q * 2^(u-127)); NVFP4 w = fl32((q * s) * g),
+ *    i.e. one rounding to fp32 after the exact product q*s and then g.
+ *  - contraction: y[b][n] = sum_k w[n][k] * x[b][k], every term and the running
+ *    sum in fp64, k ascending.  abs_y = sum_k |w * x| is returned next to it
+ *    for the acceptance bound |y_gpu - y| <= 1e-5 * abs_y + 1e-6.
+ *  - MoE: y[t][s][:] = W[ids[t][s]] . x_ts with x_ts = x[t] (x shared by a
+ *    token's slots) or x[t][s] (one x per slot).  An id outside [0, E) gives
+ *    a NaN row, which is also what the HIP library documents.
+ *
+ * Conversions from double to float follow IEC 60559 (C Annex F): round to
+ * nearest even, overflow to infinity, gradual underflow.  Build without
+ * -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_MXFP4 = 1, ORC_MXFP8 = 2, ORC_NVFP4 = 3 };
+
+/* ---- element formats ------------------------------------------------------ */
+
+/* E2M1: sign s, 2-bit exponent e (bias 1), 1-bit mantissa m.  e == 0 is the
+ * subnormal range: 0.5*m.  Otherwise 2^(e-1) * (1 + m/2). */
+double orc_e2m1(unsigned c)
+{
+    unsigned s = (c >> 3) & 1u, e = (c >> 1) & 3u, m = c & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0: an unsigned power-of-two exponent with bias 127; 0xFF is NaN. */
+double orc_e8m0(unsigned u)
+{
+    u &= 0xFFu;
+    if (u == 255u) return NAN;
+    return ldexp(1.0, (int)u - 127);
+}
+
+/* E4M3, OCP "FN" variant: bias 7, no infinities, S.1111.111 is NaN,
+ * e == 0 is subnormal: 2^-6 * m/8. */
+double orc_e4m3(unsigned b)
+{
+    unsigned s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+    double mag;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0) mag = ldexp((double)m / 8.0, -6);
+    else mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -mag : mag;
+}
+
+/* bf16 bit pattern -> exact value. */
+double orc_bf16(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int orc_block(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+
+static int64_t orc_code_bytes(int fmt, int64_t k) { return fmt == ORC_MXFP8 ? k : k / 2; }
+
+/* Decoded fp32 value of element k of one weight row. */
+static float orc_weight(int fmt, const uint8_t *codes_row, const uint8_t *scales_row, float g, int64_t k)
+{
+    double q, s;
+    if (fmt == ORC_MXFP8) {
+        q = orc_e4m3(codes_row[k]);
+    } else {
+        unsigned byte = codes_row[k / 2];
+        unsigned nib = (k % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+        q = orc_e2m1(nib);
+    }
+    if (fmt == ORC_NVFP4) {
+        s = orc_e4m3(scales_row[k / 16]);
+        return (float)((q * s) * (double)g);
+    }
+    s = orc_e8m0(scales_row[k / 32]);
+    return (float)(q * s);
+}
+
+/* ---- public entry points ---------------------------------------------------- */
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* w[r][k] = decoded fp32 weight.  g: NVFP4 per-tensor scale (pointer to one
+ * float), ignored for MX formats. */
+void orc_dequant(int fmt, const uint8_t *codes, const uint8_t *scales, const float *g,
+                 int64_t rows, int64_t k, float *w)
+{
+    const int64_t cb = orc_code_bytes(fmt, k), sb = k / orc_block(fmt);
+    const float gv = (fmt == ORC_NVFP4) ? g[0] : 1.0f;
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < k; ++j)
+            w[r * k + j] = orc_weight(fmt, codes + r * cb, scales + r * sb, gv, j);
+}
+
+/* One output: sum over k ascending, fp64. */
+static void orc_dot(int fmt, const uint8_t *codes_row, const uint8_t *scales_row, float g,
+                    const uint16_t *x, int64_t k, double *y, double *abs_y)
+{
+    double acc = 0.0, aacc = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+        double t = (double)orc_weight(fmt, codes_row, scales_row, g, j) * orc_bf16(x[j]);
+        acc += t;
+        aacc += fabs(t);
+    }
+    *y = acc;
+    *abs_y = aacc;
+}
+
+/* y[b][r] = sum_k W[r][k] * x[b][k] for b < batch, r < n. */
+void orc_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *g,
+              const uint16_t *x, int64_t batch, int64_t n, int64_t k, double *y, double *abs_y)
+{
+    const int64_t cb = orc_code_bytes(fmt, k), sb = k / orc_block(fmt);
+    const float gv = (fmt == ORC_NVFP4) ? g[0] : 1.0f;
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r)
+        for (int64_t b = 0; b < batch; ++b)
+            orc_dot(fmt, codes + r * cb, scales + r * sb, gv, x + b * k, k, &y[b * n + r], &abs_y[b * n + r]);
+}
+
+/* y[t][s][r] = sum_k W[ids[t][s]][r][k] * x_ts[k];
+ * x_ts = x[t] when x_per_slot == 0, else x[t][s].  g: [experts] for NVFP4. */
+void orc_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *g,
+                  const int32_t *ids, const uint16_t *x, int x_per_slot,
+                  int64_t experts, int64_t n, int64_t k, int64_t tokens, int64_t topk,
+                  double *y, double *abs_y)
+{
+    const int64_t cb = orc_code_bytes(fmt, k), sb = k / orc_block(fmt);
+    const int64_t pairs = tokens * topk;
+    int64_t p;
+#pragma omp parallel for schedule(static)
+    for (p = 0; p < pairs; ++p) {
+        const int64_t t = p / topk;
+        const int64_t e = ids[p];
+        const uint16_t *xv = x_per_slot ? x + p * k : x + t * k;
+        for (int64_t r = 0; r < n; ++r) {
+            if (e < 0 || e >= experts) {
+                y[p * n + r] = NAN;
+                abs_y[p * n + r] = NAN;
+                continue;
+            }
+            const float gv = (fmt == ORC_NVFP4) ? g[e] : 1.0f;
+            orc_dot(fmt, codes + (e * n + r) * cb, scales + (e * n + r) * sb, gv, xv, k,
+                    &y[p * n + r], &abs_y[p * n + r]);
+        }
+    }
+}
+
+/* Y[i][r] = sum_k X[rows[i]][k] * W[r][k] for the listed token rows only. */
+void orc_gemm_rows(int fmt, const uint8_t *codes, const uint8_t *scales, const float *g,
+                   const uint16_t *X, const int64_t *rows, int64_t nrows, int64_t n, int64_t k,
+                   double *Y, double *abs_Y)
+{
+    const int64_t cb = orc_code_bytes(fmt, k), sb = k / orc_block(fmt);
+    const float gv = (fmt == ORC_NVFP4) ? g[0] : 1.0f;
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r)
+        for (int64_t i = 0; i < nrows; ++i)
+            orc_dot(fmt, codes + r * cb, scales + r * sb, gv, X + rows[i] * k, k,
+                    &Y[i * n + r], &abs_Y[i * n + r]);
+}

@@ -1,0 +1,67 @@
+"""Plant plausible mistakes in copies of the C oracle (on the CPU) and check
+that the pin suite rejects every one of them."""
+import ctypes
+import os
+import subprocess
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+import oracle_pins as pins  # noqa: E402
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "nibble_order": ("(k % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4)", "(k % 2 == 1) ? (byte & 0x0Fu) : (byte >> 4)"),
+    "e2m1_bias": ("ldexp(1.0 + 0.5 * (double)m, (int)e - 1)", "ldexp(1.0 + 0.5 * (double)m, (int)e - 2)"),
+    "e2m1_subnormal": ("0.5 * (double)m :", "1.0 * (double)m :"),
+    "e2m1_sign": ("double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);\n    return s ? -mag : mag;",
+                  "double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);\n    return mag;"),
+    "e8m0_bias": ("ldexp(1.0, (int)u - 127)", "ldexp(1.0, (int)u - 126)"),
+    "e4m3_bias": ("ldexp(1.0 + (double)m / 8.0, (int)e - 7)", "ldexp(1.0 + (double)m / 8.0, (int)e - 8)"),
+    "e4m3_subnormal": ("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    "mx_scale_index": ("orc_e8m0(scales_row[k / 32])", "orc_e8m0(scales_row[k / 16])"),
+    "nv_scale_index": ("orc_e4m3(scales_row[k / 16])", "orc_e4m3(scales_row[k / 32])"),
+    "nv_global_dropped": ("(q * s) * (double)g", "(q * s)"),
+    "dropped_term": ("for (int64_t j = 0; j < k; ++j) {\n        double t", "for (int64_t j = 0; j < k - 1; ++j) {\n        double t"),
+    "abs_sum": ("aacc += fabs(t);", "aacc += t;"),
+    "moe_x_index": ("x_per_slot ? x + p * k : x + t * k", "x_per_slot ? x + t * k : x + p * k"),
+    "moe_expert_row": ("codes + (e * n + r) * cb", "codes + (r) * cb"),
+    "gemm_row_index": ("X + rows[i] * k", "X + i * k"),
+    "gemv_output_transposed": ("x + b * k, k, &y[b * n + r], &abs_y[b * n + r]", "x + b * k, k, &y[r * batch + b], &abs_y[r * batch + b]"),
+    "bf16_shift": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
+}
+
+
+def _build_mutant(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/present"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib), str(path), "-lm"],
+                   check=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(tmp_path, monkeypatch, name):
+    path = _build_mutant(tmp_path, name)
+    real = oracle._load()
+    mutant = ctypes.CDLL(path)
+    for attr in ("orc_e2m1", "orc_e8m0", "orc_e4m3", "orc_bf16", "orc_num_threads", "orc_set_num_threads",
+                 "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows"):
+        fr, fm = getattr(real, attr), getattr(mutant, attr)
+        fm.argtypes, fm.restype = fr.argtypes, fr.restype
+    monkeypatch.setattr(oracle, "_lib", mutant)
+    failed = []
+    for cname, check in pins.all_checks():
+        try:
+            check()
+        except AssertionError:
+            failed.append(cname)
+    assert failed, f"mutant {name} passed every pin"
