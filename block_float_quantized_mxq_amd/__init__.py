@@ -1,0 +1,205 @@
+"""Python binding of libmxq: block-float (MXFP4 / MXFP8 / NVFP4) quantized GEMV,
+expert-indexed MoE GEMV and prefill GEMM on AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmxq.so`` behind the C ABI in ``include/mxq.h``.  PyTorch
+supplies device memory and the current stream.  There is no fallback: if the
+library is missing or the device is not gfx950 the calls raise.
+
+Tensors:
+  codes   uint8, [n, k/2] (E2M1) or [n, k] (E4M3); MoE banks [E, n, ...]
+  scales  uint8, [n, k/32] (E8M0) or [n, k/16] (E4M3 for NVFP4)
+  x       bfloat16, [batch, k] (or [tokens, topk, k] for per-slot MoE input)
+  global_scale  float32 [1] (dense NVFP4) or [E] (MoE NVFP4), None for MX
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+MXFP4, MXFP8, NVFP4 = 1, 2, 3
+FORMATS = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
+BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
+OUT_F32, OUT_BF16 = 0, 1
+STATUS = {0: "MXQ_OK", 1: "MXQ_E_NULLPTR", 2: "MXQ_E_SHAPE", 3: "MXQ_E_ALIGN", 4: "MXQ_E_FORMAT",
+          5: "MXQ_E_UNSUPPORTED", 6: "MXQ_E_DEVICE", 7: "MXQ_E_LAUNCH"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxq.so")
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mxq_gemv.argtypes = [I, P, P, P, P, P, I64, I64, I64, P]
+        L.mxq_moe_gemv.argtypes = [I, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
+        L.mxq_gemm.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, P]
+        L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
+        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant):
+            f.restype = I
+        L.mxq_status_string.argtypes = [I]
+        L.mxq_status_string.restype = ctypes.c_char_p
+        L.mxq_abi_version.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mxq_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check(st, what):
+    if st != 0:
+        raise MxqError(st, what)
+
+
+def _k_of(fmt, codes):
+    return codes.shape[-1] if fmt == MXFP8 else 2 * codes.shape[-1]
+
+
+def _check_weight(fmt, codes, scales, global_scale, experts=None):
+    """Host-side shape checks: the C ABI takes raw pointers and cannot see sizes."""
+    if fmt not in BLOCK:
+        raise ValueError(f"unknown format {fmt}")
+    lead = 2 if experts is not None else 1
+    if codes.dim() != lead + 1 or scales.dim() != lead + 1:
+        raise ValueError(f"codes and scales must have {lead + 1} dimensions")
+    k = _k_of(fmt, codes)
+    if k % BLOCK[fmt]:
+        raise ValueError(f"k={k} is not a multiple of the block size {BLOCK[fmt]}")
+    if tuple(scales.shape) != tuple(codes.shape[:-1]) + (k // BLOCK[fmt],):
+        raise ValueError(f"scales shape {tuple(scales.shape)} does not match codes {tuple(codes.shape)}")
+    if (global_scale is None) != (fmt != NVFP4):
+        raise ValueError("NVFP4 needs global_scale; MX formats take none")
+    if global_scale is not None and global_scale.numel() < (experts if experts is not None else 1):
+        raise ValueError("global_scale has too few elements")
+    return k
+
+
+def gemv(fmt, codes, scales, x, global_scale=None, out=None, stream=None):
+    """y[b][i] = sum_k W[i][k] * x[b][k] -> float32 [batch, n]."""
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    x = _dev(x, torch.bfloat16, "x")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    k = _check_weight(fmt, codes, scales, global_scale)
+    n = codes.shape[0]
+    x2 = x.reshape(-1, x.shape[-1])
+    if x2.shape[1] != k:
+        raise ValueError(f"x has k={x2.shape[1]}, weights have k={k}")
+    batch = x2.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=codes.device)
+    out = _dev(out, torch.float32, "out")
+    if out.numel() != batch * n:
+        raise ValueError("out must hold batch * n elements")
+    _check(lib().mxq_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x2), _ptr(out), n, k, batch,
+                          _stream(stream)), "mxq_gemv")
+    return out
+
+
+def moe_gemv(fmt, codes, scales, expert_ids, x, x_per_slot, global_scale=None, out=None, stream=None):
+    """y[t][s][i] = sum_k W[ids[t][s]][i][k] * x_ts[k] -> float32 [tokens, topk, n]."""
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    expert_ids = _dev(expert_ids, torch.int32, "expert_ids")
+    x = _dev(x, torch.bfloat16, "x")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    experts, n = codes.shape[0], codes.shape[1]
+    k = _check_weight(fmt, codes, scales, global_scale, experts=experts)
+    if expert_ids.dim() != 2:
+        raise ValueError("expert_ids must be [tokens, topk]")
+    tokens, topk = expert_ids.shape
+    want = (tokens, topk, k) if x_per_slot else (tokens, k)
+    if tuple(x.shape) != want:
+        raise ValueError(f"x must have shape {want}, got {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((tokens, topk, n), dtype=torch.float32, device=codes.device)
+    out = _dev(out, torch.float32, "out")
+    if out.numel() != tokens * topk * n:
+        raise ValueError("out must hold tokens * topk * n elements")
+    _check(lib().mxq_moe_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(expert_ids), _ptr(x),
+                              1 if x_per_slot else 0, _ptr(out), experts, n, k, tokens, topk, _stream(stream)),
+           "mxq_moe_gemv")
+    return out
+
+
+def gemm(fmt, codes, scales, x, global_scale=None, out_dtype=torch.bfloat16, out=None, stream=None):
+    """Y[m][i] = sum_k X[m][k] * W[i][k] -> [m, n] in float32 or bfloat16 (RNE)."""
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    x = _dev(x, torch.bfloat16, "x")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    k = _check_weight(fmt, codes, scales, global_scale)
+    n = codes.shape[0]
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}], got {tuple(x.shape)}")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=codes.device)
+    out = _dev(out, out_dtype, "out")
+    if out.numel() != m * n:
+        raise ValueError("out must hold m * n elements")
+    ydt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    _check(lib().mxq_gemm(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x), _ptr(out), ydt, m, n, k,
+                          _stream(stream)), "mxq_gemm")
+    return out
+
+
+def dequant(fmt, codes, scales, global_scale=None, out=None, stream=None):
+    """Decoded fp32 weights [rows, k] (same device decode as the other kernels)."""
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    k = _check_weight(fmt, codes, scales, global_scale)
+    rows = codes.shape[0]
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.float32, device=codes.device)
+    out = _dev(out, torch.float32, "out")
+    if out.numel() != rows * k:
+        raise ValueError("out must hold rows * k elements")
+    _check(lib().mxq_dequant(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(out), rows, k,
+                             _stream(stream)), "mxq_dequant")
+    return out
+
+
+def weight_bytes(fmt, n, k):
+    """Algorithmic bytes of one weight matrix: codes + block scales (+4 for NVFP4's fp32 scale)."""
+    codes = n * k if fmt == MXFP8 else n * k // 2
+    return codes + n * (k // BLOCK[fmt]) + (4 if fmt == NVFP4 else 0)

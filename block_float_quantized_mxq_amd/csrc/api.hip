@@ -1,0 +1,177 @@
+// api.hip -- the C ABI declared in include/mxq.h: host-side validation, the
+// gfx950 device check, kernel-configuration choice and launch.
+//
+// Validation happens before any HIP call, so argument errors are reported on
+// machines without a GPU as well.  Checks run in the order the header lists
+// (format, null pointers, shapes, alignment, supported sizes, device).
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mxq.h"
+#include "kernels.hpp"
+
+#define MXQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using mxq::kMXFP4;
+using mxq::kMXFP8;
+using mxq::kNVFP4;
+
+bool valid_fmt(int fmt) { return fmt == kMXFP4 || fmt == kMXFP8 || fmt == kNVFP4; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Per-device result of the gfx950 check: 0 unknown, 1 ok, 2 not usable.
+std::atomic<int> g_device_ok[64];
+
+mxq_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return MXQ_E_DEVICE;
+    }
+    if (dev >= 64) return MXQ_E_DEVICE;
+    int state = g_device_ok[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return MXQ_E_DEVICE;
+        }
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_ok[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? MXQ_OK : MXQ_E_DEVICE;
+}
+
+mxq_status_t check_weight(int fmt, const uint8_t* codes, const uint8_t* scales, const float* gscale) {
+    if (!valid_fmt(fmt)) return MXQ_E_FORMAT;
+    if ((fmt == kNVFP4) != (gscale != nullptr)) return MXQ_E_FORMAT;
+    if (!codes || !scales) return MXQ_E_NULLPTR;
+    return MXQ_OK;
+}
+
+mxq_status_t check_k(int fmt, int64_t k) {
+    if (k <= 0 || k % mxq::block_elems(fmt) != 0) return MXQ_E_SHAPE;
+    return MXQ_OK;
+}
+
+mxq_status_t launched(bool ok) {
+    if (!ok) return MXQ_E_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_E_LAUNCH;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+namespace mxq {
+
+// Kernel configuration for a dense GEMV, chosen from the shape so that the grid
+// holds enough workgroups to cover all 256 CUs several times while every lane
+// still streams several chunks.  MXQ_GEMV_CONFIG="g,s,r" overrides the choice
+// (used only to compare variants when tuning).
+GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
+    if (const char* env = std::getenv("MXQ_GEMV_CONFIG")) {
+        GemvConfig c{0, 0, 0};
+        if (std::sscanf(env, "%d,%d,%d", &c.g, &c.s, &c.r) == 3) return c;
+    }
+    const int64_t cb = (code_bytes_per_row(fmt, k) % 16 == 0) ? 16 : 8;
+    const int64_t nchunks = code_bytes_per_row(fmt, k) / cb;
+    if (nchunks < 16) return nchunks >= 8 ? GemvConfig{8, 1, 1} : GemvConfig{4, 1, 1};
+    const int64_t target_wgs = 1024;
+    // Rows per workgroup for (16, s, r) is (16 / s) * r.
+    if (batch <= 2 && n / 64 >= target_wgs / 2) return GemvConfig{16, 1, 4};
+    if (n / 16 >= target_wgs / 2) return GemvConfig{16, 1, 1};
+    if (n / 8 >= target_wgs / 2 && nchunks >= 64) return GemvConfig{16, 2, 1};
+    if (n / 4 >= target_wgs / 2 && nchunks >= 128) return GemvConfig{16, 4, 1};
+    if (n / 2 >= target_wgs / 2 && nchunks >= 256) return GemvConfig{16, 8, 1};
+    if (nchunks >= 512) return GemvConfig{16, 16, 1};
+    return GemvConfig{16, 1, 1};
+}
+
+}  // namespace mxq
+
+MXQ_API const char* mxq_status_string(int s) {
+    switch (s) {
+        case MXQ_OK: return "ok";
+        case MXQ_E_NULLPTR: return "a required pointer is NULL";
+        case MXQ_E_SHAPE: return "invalid size (non-positive, or k not a multiple of the block size)";
+        case MXQ_E_ALIGN: return "pointer not aligned (codes/activations 16 bytes, outputs/ids/scale 4 bytes)";
+        case MXQ_E_FORMAT: return "invalid format, output type, or global_scale presence";
+        case MXQ_E_UNSUPPORTED: return "size above the supported maximum";
+        case MXQ_E_DEVICE: return "current device is not a gfx950 GPU";
+        case MXQ_E_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+MXQ_API int mxq_abi_version(void) { return 1; }
+
+MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                              const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (!x || !y) return MXQ_E_NULLPTR;
+    if (n <= 0 || batch <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
+    if (n > kMaxDim || k > kMaxDim || batch > MXQ_MAX_BATCH) return MXQ_E_UNSUPPORTED;
+    if ((st = check_device()) != MXQ_OK) return st;
+    const mxq::GemvArgs a{fmt, codes, scales, global_scale, x, y, n, k, batch};
+    return launched(mxq::launch_gemv(a, mxq::choose_gemv_config(fmt, n, k, batch), as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_moe_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                  const int32_t* expert_ids, const uint16_t* x, int x_per_slot, float* y,
+                                  int64_t num_experts, int64_t n, int64_t k, int64_t tokens, int64_t topk,
+                                  void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (!expert_ids || !x || !y) return MXQ_E_NULLPTR;
+    if (num_experts <= 0 || n <= 0 || tokens <= 0 || topk <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(expert_ids, 4) ||
+        !aligned(global_scale, 4))
+        return MXQ_E_ALIGN;
+    if (n > kMaxDim || k > kMaxDim || num_experts > kMaxDim || tokens > MXQ_MAX_BATCH || topk > MXQ_MAX_TOPK)
+        return MXQ_E_UNSUPPORTED;
+    if ((st = check_device()) != MXQ_OK) return st;
+    const mxq::MoeArgs a{fmt, codes, scales, global_scale, expert_ids, x, x_per_slot ? 1 : 0, y,
+                         num_experts, n, k, tokens, topk};
+    return launched(mxq::launch_moe(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                              const uint16_t* x, void* y, int y_dtype, int64_t m, int64_t n, int64_t k,
+                              void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (y_dtype != MXQ_OUT_F32 && y_dtype != MXQ_OUT_BF16) return MXQ_E_FORMAT;
+    if (!x || !y) return MXQ_E_NULLPTR;
+    if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return MXQ_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
+    if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return MXQ_E_UNSUPPORTED;
+    if ((st = check_device()) != MXQ_OK) return st;
+    const mxq::GemmArgs a{fmt, codes, scales, global_scale, x, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k};
+    return launched(mxq::launch_gemm(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                 float* w, int64_t rows, int64_t k, void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (!w) return MXQ_E_NULLPTR;
+    if (rows <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
+    if (!aligned(codes, 16) || !aligned(w, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
+    if (rows > kMaxDim || k > kMaxDim) return MXQ_E_UNSUPPORTED;
+    if ((st = check_device()) != MXQ_OK) return st;
+    const mxq::DequantArgs a{fmt, codes, scales, global_scale, w, rows, k};
+    return launched(mxq::launch_dequant(a, as_stream(stream)));
+}

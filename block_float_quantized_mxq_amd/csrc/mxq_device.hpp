@@ -1,0 +1,106 @@
+// mxq_device.hpp -- device-side building blocks shared by the libmxq kernels:
+// in-register decode of E2M1 / E4M3 codes and E8M0 / E4M3 block scales, the
+// bf16 dot product, and wave64 cross-lane sums.
+//
+// Decode follows the "Decoding block-float formats in software" section of the
+// "MLxcel 0.8 release" post (and slide 12 of the Strix Halo talk): codes are
+// turned into 16-bit floats inside the kernel, exactly, and then multiplied
+// with the activations.  On gfx950 the conversion is one hardware instruction
+// per two codes (V_CVT_SCALEF32_PK_BF16_FP4 / _FP8 with a unit scale), which
+// replaces the pages' bit-placement trick: every E2M1 and every finite E4M3
+// value is exactly representable in bf16, so the conversion is exact.  The
+// block scale is applied once per block partial sum in fp32 instead of per
+// element.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "formats.hpp"
+
+namespace mxq {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Elements per scale block.
+template <int FMT> struct BlockSize { static constexpr int value = (FMT == kNVFP4) ? 16 : 32; };
+
+
+// ---- code decode: packed codes -> bf16 pairs (element 2j in the low half) ----
+
+// Byte `SEL` of `w` holds two E2M1 codes (even element in bits 3:0).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// Half-word `HI` of `w` holds two E4M3 codes (even element in the low byte).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Decode DW code dwords into bf16 pairs: 4 pairs per dword for E2M1, 2 for E4M3.
+template <int FMT, int DW>
+__device__ __forceinline__ void decode_dwords(const uint32_t (&c)[DW], uint32_t (&p)[(FMT == kMXFP8) ? 2 * DW : 4 * DW]) {
+#pragma unroll
+    for (int d = 0; d < DW; ++d) {
+        if constexpr (FMT == kMXFP8) {
+            p[2 * d + 0] = fp8x2_to_bf16x2<false>(c[d]);
+            p[2 * d + 1] = fp8x2_to_bf16x2<true>(c[d]);
+        } else {
+            p[4 * d + 0] = fp4x2_to_bf16x2<0>(c[d]);
+            p[4 * d + 1] = fp4x2_to_bf16x2<1>(c[d]);
+            p[4 * d + 2] = fp4x2_to_bf16x2<2>(c[d]);
+            p[4 * d + 3] = fp4x2_to_bf16x2<3>(c[d]);
+        }
+    }
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
+
+// ---- block scales -------------------------------------------------------------
+
+// E8M0 byte u -> 2^(u-127) as fp32 (u = 0 gives the subnormal 2^-127); 0xFF -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t u) {
+    float v = __builtin_amdgcn_ldexpf(1.0f, (int)u - 127);
+    return (u == 255u) ? __builtin_nanf("") : v;
+}
+
+// E4M3 (OCP) byte -> fp32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
+// ---- arithmetic -------------------------------------------------------------------
+
+// c + a.lo*b.lo + a.hi*b.hi with bf16 inputs and fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+// DPP controls (GFX9 encoding).
+enum : int { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G in {1,2,4,8,16,32,64}); every lane of a
+// group ends with the group total.  The order of additions is fixed.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += dpp_f32<kDppQuadXor1>(v);
+    if constexpr (G >= 4) v += dpp_f32<kDppQuadXor2>(v);
+    if constexpr (G >= 8) v += dpp_f32<kDppRowHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp_f32<kDppRowMirror>(v);
+    if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+}  // namespace mxq

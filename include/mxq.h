@@ -1,0 +1,167 @@
+/*
+ * mxq.h -- C ABI of libmxq: block-float quantized GEMV, expert-indexed MoE
+ * GEMV and prefill GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * The operation all entry points share is the one the "MLxcel 0.8 release"
+ * post (backend.ai) describes in its section "Decoding block-float formats in
+ * software", and slide 7 of the talk "High-performance LLM/VLM inference on
+ * AMD Strix Halo with mlxcel engine" restates: weights stored as MXFP4, MXFP8
+ * or NVFP4 blocks are unpacked to floating point inside the kernel and then
+ * contracted with the activations.  Decode is exact (same section, and slide
+ * 12 of the talk).  Decode speed is bounded by how fast the weights stream from
+ * memory ("The memory wall" section of the post, slide 15 of the talk).
+ *
+ * Formats (OCP Microscaling v1.0 and NVFP4 public definitions; the pages give
+ * the names and the E2M1 field widths only):
+ *   MXFP4  32 E2M1 codes + one E8M0 block scale            (4.25 bits/weight)
+ *   MXFP8  32 E4M3 codes (OCP "FN") + one E8M0 block scale (8.25 bits/weight)
+ *   NVFP4  16 E2M1 codes + one E4M3 block scale, plus one fp32 scale per
+ *          tensor (per expert in an MoE bank)                (4.5 bits/weight)
+ *
+ * Layout of a weight W[n][k] (n outputs, k the reduction dimension):
+ *   codes  uint8 [n][k/2] for E2M1: byte j of a row holds element 2j in bits
+ *          3:0 and element 2j+1 in bits 7:4;  uint8 [n][k] for E4M3.
+ *   scales uint8 [n][k/32] (E8M0) or [n][k/16] (E4M3), row-major; block b of a
+ *          row covers elements [b*bs, (b+1)*bs).
+ *   An MoE bank stacks experts in front: [E][n][...].
+ * Activations are bf16 bit patterns (uint16), row-major [rows][k].
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates and frees nothing and keeps no pointer after it returns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  MXQ_OK means "validated and enqueued".
+ *   - Arguments are validated on the host before anything is enqueued; the
+ *     first failing check is returned and nothing runs:
+ *       MXQ_E_FORMAT       unknown format, or global_scale given for an MX
+ *                          format / missing for NVFP4, or unknown output type
+ *       MXQ_E_NULLPTR      a required pointer is NULL
+ *       MXQ_E_SHAPE        a size <= 0, or k not a multiple of the block size
+ *                          (32 for MX formats, 16 for NVFP4)
+ *       MXQ_E_ALIGN        codes or activations not 16-byte aligned, outputs,
+ *                          expert ids or global_scale not 4-byte aligned
+ *       MXQ_E_UNSUPPORTED  a size above the documented maximum
+ *       MXQ_E_DEVICE       the current device is not a gfx950 GPU (or there is
+ *                          no device)
+ *       MXQ_E_LAUNCH       the kernel launch itself failed
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Offsets are computed in 64-bit arithmetic throughout.
+ *   - Thread-safe and reentrant; no global mutable state besides a per-device
+ *     capability cache filled once.  The library never prints.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     on every run (fixed reduction order, no atomics).
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MXQ_FMT_MXFP4 = 1, MXQ_FMT_MXFP8 = 2, MXQ_FMT_NVFP4 = 3 } mxq_format_t;
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_E_NULLPTR = 1,
+    MXQ_E_SHAPE = 2,
+    MXQ_E_ALIGN = 3,
+    MXQ_E_FORMAT = 4,
+    MXQ_E_UNSUPPORTED = 5,
+    MXQ_E_DEVICE = 6,
+    MXQ_E_LAUNCH = 7
+} mxq_status_t;
+
+typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_t;
+
+/* Largest batch of the GEMV and largest token count of the MoE GEMV. */
+#define MXQ_MAX_BATCH 8
+/* Largest number of routed experts per token. */
+#define MXQ_MAX_TOPK 16
+
+/*
+ * Dense GEMV (the decode projection; "Decoding block-float formats in
+ * software" and "Profiling set the porting order" sections of the post, where
+ * the quantized matrix-vector kernel takes 95% of dense decode time):
+ *
+ *   y[b][i] = sum_k W[i][k] * x[b][k]     for b < batch, i < n
+ *
+ * with W decoded exactly, products and sums in fp32, the NVFP4 per-tensor
+ * scale applied once to each output.
+ *   fmt           format of W
+ *   codes, scales W as laid out above, n rows of k elements
+ *   global_scale  NVFP4: pointer to one fp32 on the device; MX formats: NULL
+ *   x             bf16 [batch][k]
+ *   y             fp32 [batch][n] (written, never read)
+ *   n, k          1 <= n, k < 2^31; k % block == 0
+ *   batch         1 .. MXQ_MAX_BATCH
+ */
+mxq_status_t mxq_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                      const uint16_t *x, float *y, int64_t n, int64_t k, int64_t batch, void *stream);
+
+/*
+ * Expert-indexed MoE GEMV: every routed (token, slot) pair multiplies its
+ * activation vector by the weight of the expert it is routed to, and only the
+ * routed experts' weights are read, each expert once per call however many
+ * pairs route to it ("Unified memory" section of the post: a token reads only
+ * its active experts; slide 4 of the talk).  No routing weights, no combine.
+ *
+ *   y[t][s][i] = sum_k W[ids[t][s]][i][k] * x_ts[k]
+ *   x_ts = x[t]     (x_per_slot == 0: x is bf16 [tokens][k], e.g. gate/up)
+ *   x_ts = x[t][s]  (x_per_slot != 0: x is bf16 [tokens][topk][k], e.g. down)
+ *
+ *   codes, scales  the bank: [num_experts][n][...]
+ *   global_scale   NVFP4: fp32 [num_experts] on the device; MX: NULL
+ *   expert_ids     int32 [tokens][topk] on the device.  Ids are not checked
+ *                  on the host (that would need a synchronisation); a pair
+ *                  whose id is outside [0, num_experts) gets a NaN output row.
+ *   y              fp32 [tokens][topk][n]
+ *   tokens         1 .. MXQ_MAX_BATCH;  topk 1 .. MXQ_MAX_TOPK
+ */
+mxq_status_t mxq_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                          const int32_t *expert_ids, const uint16_t *x, int x_per_slot, float *y,
+                          int64_t num_experts, int64_t n, int64_t k, int64_t tokens, int64_t topk,
+                          void *stream);
+
+/*
+ * Prefill GEMM on the same weights (compute bound; the post's "The memory
+ * wall" section and slide 12 of the talk: decode to 16-bit floats on the GPU,
+ * then the matrix unit):
+ *
+ *   Y[m][i] = sum_k X[m][k] * W[i][k]
+ *
+ * W is decoded to bf16 tiles (exact for every weight whose value is a normal
+ * bf16 or zero, which holds for E8M0 exponents in [3, 250] with any code) and
+ * multiplied on the bf16 matrix cores with fp32 accumulation; the NVFP4
+ * per-tensor scale multiplies the fp32 result.
+ *   x       bf16 [m][k]
+ *   y       [m][n], fp32 (y_dtype MXQ_OUT_F32) or bf16 rounded to nearest even
+ *           from the fp32 result (MXQ_OUT_BF16)
+ *   m, n, k >= 1, < 2^31; k % 32 == 0 for every format
+ */
+mxq_status_t mxq_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                      const uint16_t *x, void *y, int y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
+
+/*
+ * Decoded weights, for checking the in-kernel decode bit for bit:
+ *   w[r][j] = fl32(q * 2^(u-127))        MX formats
+ *   w[r][j] = fl32((q * s) * g)          NVFP4 (q*s is exact; one rounding)
+ * with q the decoded code, u the E8M0 byte, s the decoded E4M3 block scale and
+ * g the per-tensor scale.  Uses the same device decode as the other kernels.
+ *   w   fp32 [rows][k]
+ */
+mxq_status_t mxq_dequant(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                         float *w, int64_t rows, int64_t k, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *mxq_status_string(int status);
+
+/* ABI version of this header: 1. */
+int mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -42,6 +42,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -201,17 +202,34 @@ void orc_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const fl
     }
 }
 
-/* Y[i][r] = sum_k X[rows[i]][k] * W[r][k] for the listed token rows only. */
+/* Y[i][r] = sum_k X[rows[i]][k] * W[r][k] for the listed token rows only.
+ * Each weight row is decoded once into fp32 and then summed against every
+ * listed token row in ascending k, in fp64 (the same definition as orc_dot). */
 void orc_gemm_rows(int fmt, const uint8_t *codes, const uint8_t *scales, const float *g,
                    const uint16_t *X, const int64_t *rows, int64_t nrows, int64_t n, int64_t k,
                    double *Y, double *abs_Y)
 {
     const int64_t cb = orc_code_bytes(fmt, k), sb = k / orc_block(fmt);
     const float gv = (fmt == ORC_NVFP4) ? g[0] : 1.0f;
-    int64_t r;
-#pragma omp parallel for schedule(static)
-    for (r = 0; r < n; ++r)
-        for (int64_t i = 0; i < nrows; ++i)
-            orc_dot(fmt, codes + r * cb, scales + r * sb, gv, X + rows[i] * k, k,
-                    &Y[i * n + r], &abs_Y[i * n + r]);
+#pragma omp parallel
+    {
+        float *w = (float *)malloc((size_t)k * sizeof(float));
+        int64_t r;
+#pragma omp for schedule(static)
+        for (r = 0; r < n; ++r) {
+            for (int64_t j = 0; j < k; ++j) w[j] = orc_weight(fmt, codes + r * cb, scales + r * sb, gv, j);
+            for (int64_t i = 0; i < nrows; ++i) {
+                const uint16_t *xr = X + rows[i] * k;
+                double acc = 0.0, aacc = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    double t = (double)w[j] * orc_bf16(xr[j]);
+                    acc += t;
+                    aacc += fabs(t);
+                }
+                Y[i * n + r] = acc;
+                abs_Y[i * n + r] = aacc;
+            }
+        }
+        free(w);
+    }
 }

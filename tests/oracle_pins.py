@@ -229,6 +229,7 @@ def check_moe_bruteforce(fmt, x_per_slot):
                 continue
             for r in range(n):
                 assert bf.close(y[t, s, r], ex[t][s][r], k), (fmt, t, s, r)
+                assert bf.close(a[t, s, r], (ex[t][s][r][1], ex[t][s][r][1]), k), (fmt, t, s, r)
 
 
 def check_gemm_rows_bruteforce(fmt):
@@ -244,6 +245,7 @@ def check_gemm_rows_bruteforce(fmt):
         for c in range(n):
             ex = bf.dot_exact(fmt, codes[c], scales[c], g0, X[rr], k)
             assert bf.close(Y[i, c], ex, k), (fmt, i, c)
+            assert bf.close(A[i, c], (ex[1], ex[1]), k), (fmt, i, c)
 
 
 def all_checks():

@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/mxq.h declares, and rejects bad arguments on the host (validation runs
+before any HIP call, so bogus-but-aligned pointer values are never touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+import block_float_quantized_mxq_amd as mxq  # noqa: E402
+
+OK, NULLPTR, SHAPE, ALIGN, FORMAT, UNSUPPORTED, DEVICE = 0, 1, 2, 3, 4, 5, 6
+A = 0x10000  # aligned fake device address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mxq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_status_string", "mxq_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mxq.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", mxq.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\b(mxq_\w+)\b", out.stdout))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.mxq_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(8):
+        assert mxq.status_string(s)
+    assert mxq.status_string(99) == "unknown status"
+
+
+def gemv(fmt=1, codes=A, scales=A, g=None, x=A, y=A, n=8, k=64, batch=1):
+    return mxq.lib().mxq_gemv(fmt, codes, scales, g, x, y, n, k, batch, None)
+
+
+def moe(fmt=1, codes=A, scales=A, g=None, ids=A, x=A, per=0, y=A, E=4, n=8, k=64, T=1, topk=2):
+    return mxq.lib().mxq_moe_gemv(fmt, codes, scales, g, ids, x, per, y, E, n, k, T, topk, None)
+
+
+def gemm(fmt=1, codes=A, scales=A, g=None, x=A, y=A, ydt=0, m=4, n=8, k=64):
+    return mxq.lib().mxq_gemm(fmt, codes, scales, g, x, y, ydt, m, n, k, None)
+
+
+def deq(fmt=1, codes=A, scales=A, g=None, w=A, rows=4, k=64):
+    return mxq.lib().mxq_dequant(fmt, codes, scales, g, w, rows, k, None)
+
+
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq])
+def test_format_errors(call):
+    assert call(fmt=0) == FORMAT
+    assert call(fmt=4) == FORMAT
+    assert call(fmt=3, g=None) == FORMAT      # NVFP4 needs its per-tensor scale
+    assert call(fmt=1, g=A) == FORMAT         # MX formats take none
+    assert call(fmt=2, g=A) == FORMAT
+
+
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq])
+def test_null_pointers(call):
+    assert call(codes=None) == NULLPTR
+    assert call(scales=None) == NULLPTR
+
+
+def test_null_pointers_per_entry():
+    assert gemv(x=None) == NULLPTR and gemv(y=None) == NULLPTR
+    assert moe(ids=None) == NULLPTR and moe(x=None) == NULLPTR and moe(y=None) == NULLPTR
+    assert gemm(x=None) == NULLPTR and gemm(y=None) == NULLPTR
+    assert deq(w=None) == NULLPTR
+
+
+def test_shape_errors():
+    for bad in (0, -1):
+        assert gemv(n=bad) == SHAPE and gemv(k=bad) == SHAPE and gemv(batch=bad) == SHAPE
+        assert moe(E=bad) == SHAPE and moe(n=bad) == SHAPE and moe(T=bad) == SHAPE and moe(topk=bad) == SHAPE
+        assert gemm(m=bad) == SHAPE and gemm(n=bad) == SHAPE and gemm(k=bad) == SHAPE
+        assert deq(rows=bad) == SHAPE and deq(k=bad) == SHAPE
+    # k must be a whole number of blocks: 32 for MX formats, 16 for NVFP4 (GEMM: 32 for all)
+    assert gemv(fmt=1, k=48) == SHAPE and gemv(fmt=2, k=16) == SHAPE
+    assert gemv(fmt=3, g=A, k=40) == SHAPE
+    assert moe(fmt=1, k=16) == SHAPE and deq(fmt=2, k=80) == SHAPE
+    assert gemm(fmt=3, g=A, k=48) == SHAPE
+
+
+def test_alignment_errors():
+    assert gemv(codes=A + 8) == ALIGN and gemv(x=A + 2) == ALIGN and gemv(y=A + 2) == ALIGN
+    assert gemv(fmt=3, g=A + 1, k=64) == ALIGN
+    assert moe(ids=A + 2) == ALIGN and moe(codes=A + 4) == ALIGN and moe(x=A + 8) == ALIGN
+    assert gemm(x=A + 4) == ALIGN and gemm(y=A + 1) == ALIGN
+    assert deq(w=A + 2) == ALIGN and deq(codes=A + 1) == ALIGN
+
+
+def test_unsupported_sizes():
+    assert gemv(batch=9) == UNSUPPORTED
+    assert gemv(n=1 << 31) == UNSUPPORTED
+    assert moe(T=9) == UNSUPPORTED and moe(topk=17) == UNSUPPORTED
+    assert gemm(m=1 << 31) == UNSUPPORTED
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is present (it would launch on fake pointers)")
+def test_device_error_without_gpu():
+    assert gemv() == DEVICE and moe() == DEVICE and gemm() == DEVICE and deq() == DEVICE
+    assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        mxq.gemv(1, torch.zeros(4, 16, dtype=torch.uint8), torch.zeros(4, 1, dtype=torch.uint8),
+                 torch.zeros(1, 32, dtype=torch.bfloat16))

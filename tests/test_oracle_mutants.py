@@ -27,10 +27,12 @@ MUTANTS = {
     "nv_scale_index": ("orc_e4m3(scales_row[k / 16])", "orc_e4m3(scales_row[k / 32])"),
     "nv_global_dropped": ("(q * s) * (double)g", "(q * s)"),
     "dropped_term": ("for (int64_t j = 0; j < k; ++j) {\n        double t", "for (int64_t j = 0; j < k - 1; ++j) {\n        double t"),
-    "abs_sum": ("aacc += fabs(t);", "aacc += t;"),
+    "abs_sum": ("aacc += fabs(t);\n    }\n    *y = acc;", "aacc += t;\n    }\n    *y = acc;"),
+    "gemm_abs_sum": ("aacc += fabs(t);\n                }", "aacc += t;\n                }"),
     "moe_x_index": ("x_per_slot ? x + p * k : x + t * k", "x_per_slot ? x + t * k : x + p * k"),
     "moe_expert_row": ("codes + (e * n + r) * cb", "codes + (r) * cb"),
     "gemm_row_index": ("X + rows[i] * k", "X + i * k"),
+    "gemm_dropped_term": ("double t = (double)w[j] * orc_bf16(xr[j]);", "double t = (j + 1 < k) ? (double)w[j] * orc_bf16(xr[j]) : 0.0;"),
     "gemv_output_transposed": ("x + b * k, k, &y[b * n + r], &abs_y[b * n + r]", "x + b * k, k, &y[r * batch + b], &abs_y[r * batch + b]"),
     "bf16_shift": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
 }
