@@ -72,27 +72,31 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 namespace mxq {
 
-// Kernel configuration for a dense GEMV, chosen from the shape so that the grid
-// holds enough workgroups to cover all 256 CUs several times while every lane
-// still streams several chunks.  MXQ_GEMV_CONFIG="g,s,r" overrides the choice
-// (used only to compare variants when tuning).
+// Dense GEMV stream settings: 64 lanes per row block (1 KB-contiguous loads)
+// when the row has at least 64 chunks, else 32 or 16; rows per group chosen so
+// that the grid holds about 432 workgroups (1.7 per CU) with a whole number of
+// blocks per group.  MXQ_GEMV_CONFIG="g,d,xl,wgs" overrides the choice (used
+// only to compare variants when tuning).
 GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
+    (void)batch;
     if (const char* env = std::getenv("MXQ_GEMV_CONFIG")) {
-        GemvConfig c{0, 0, 0};
-        if (std::sscanf(env, "%d,%d,%d", &c.g, &c.s, &c.r) == 3) return c;
+        int g = 0, d = 0, xl = 0;
+        long long wgs = 0;
+        if (std::sscanf(env, "%d,%d,%d,%lld", &g, &d, &xl, &wgs) == 4) return GemvConfig{g, d, xl, (int64_t)wgs};
     }
     const int64_t cb = (code_bytes_per_row(fmt, k) % 16 == 0) ? 16 : 8;
     const int64_t nchunks = code_bytes_per_row(fmt, k) / cb;
-    if (nchunks < 16) return nchunks >= 8 ? GemvConfig{8, 1, 1} : GemvConfig{4, 1, 1};
-    const int64_t target_wgs = 1024;
-    // Rows per workgroup for (16, s, r) is (16 / s) * r.
-    if (batch <= 2 && n / 64 >= target_wgs / 2) return GemvConfig{16, 1, 4};
-    if (n / 16 >= target_wgs / 2) return GemvConfig{16, 1, 1};
-    if (n / 8 >= target_wgs / 2 && nchunks >= 64) return GemvConfig{16, 2, 1};
-    if (n / 4 >= target_wgs / 2 && nchunks >= 128) return GemvConfig{16, 4, 1};
-    if (n / 2 >= target_wgs / 2 && nchunks >= 256) return GemvConfig{16, 8, 1};
-    if (nchunks >= 512) return GemvConfig{16, 16, 1};
-    return GemvConfig{16, 1, 1};
+    const int g = nchunks >= 64 ? 64 : (nchunks >= 32 ? 32 : 16);
+    int p = 0;
+    for (int cand : {1, 2, 4})
+        if (p == 0 && (cand * nchunks) % g == 0) p = cand;
+    if (p == 0) p = 1;
+    const int64_t per_wg = 256 / g;
+    const int64_t nblocks = (n + p - 1) / p;
+    int64_t bpg = (nblocks + 432 * per_wg / 2) / (432 * per_wg);  // blocks per group, rounded
+    if (bpg < 1) bpg = 1;
+    const int64_t wgs = (nblocks + bpg * per_wg - 1) / (bpg * per_wg);
+    return GemvConfig{g, 4, 1, wgs};
 }
 
 }  // namespace mxq

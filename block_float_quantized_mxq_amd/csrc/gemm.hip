@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two E2M1 codes (byte SEL of w) times an arbitrary fp32 scale s, as a bf16 pair.
+template <int SEL>
+__device__ __forceinline__ uint32_t scaled_fp4x2_to_bf16x2(uint32_t w, float s) {
+    const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+    const bf16x2_t b = {(__bf16)(f[0] * s), (__bf16)(f[1] * s)};
+    return __builtin_bit_cast(uint32_t, b);
+}
+
 // Decode 32 consecutive elements of one weight row, starting at element k0,
 // to bf16 (scale folded in) into 16 dwords.  Elements past k are zero.
 template <int FMT>
@@ -51,21 +59,31 @@ __device__ __forceinline__ void decode_w32(const uint8_t* crow, const uint8_t* s
         }
     } else {
         const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + k0 / 2);
-        float s0, s1;
-        if constexpr (FMT == kMXFP4) {
-            s0 = s1 = e8m0_to_f32(srow[k0 / 32]);
-        } else {
-            s0 = e4m3_to_f32(srow[k0 / 16]);
-            s1 = e4m3_to_f32(srow[k0 / 16 + 1]);
-        }
         const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+        if constexpr (FMT == kMXFP4) {
+            // E8M0 scales are powers of two: the conversion applies them exactly.
+            const float s = e8m0_to_f32(srow[k0 / 32]);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const float s = d < 2 ? s0 : s1;
-            out[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 0));
-            out[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 1));
-            out[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 2));
-            out[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 3));
+            for (int d = 0; d < 4; ++d) {
+                out[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 0));
+                out[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 1));
+                out[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 2));
+                out[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], s, 3));
+            }
+        } else {
+            // The conversion instruction uses only the exponent of its scale operand,
+            // so E4M3 block scales (which carry mantissa bits) are applied in fp32:
+            // q * s has at most 6 significant bits, so the bf16 result is exact.
+            const float s0 = e4m3_to_f32(srow[k0 / 16]);
+            const float s1 = e4m3_to_f32(srow[k0 / 16 + 1]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const float s = d < 2 ? s0 : s1;
+                out[4 * d + 0] = scaled_fp4x2_to_bf16x2<0>(w[d], s);
+                out[4 * d + 1] = scaled_fp4x2_to_bf16x2<1>(w[d], s);
+                out[4 * d + 2] = scaled_fp4x2_to_bf16x2<2>(w[d], s);
+                out[4 * d + 3] = scaled_fp4x2_to_bf16x2<3>(w[d], s);
+            }
         }
     }
 }

@@ -1,0 +1,10 @@
+// gemv_mxfp8.hip -- MXFP8 instances of the dense GEMV (gemv_impl.hpp).
+#include "gemv_impl.hpp"
+
+namespace mxq {
+
+bool launch_gemv_mxfp8(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
+    return launch_gemv_cb<kMXFP8, 16>(a, cfg, st);
+}
+
+}  // namespace mxq

@@ -19,23 +19,16 @@ struct GemvArgs {
     int64_t n, k, batch;
 };
 
-// Lanes per row group (g), groups splitting one row's chunks (s), rows per
-// group (r).  Only the combinations listed in MXQ_GEMV_CONFIGS are compiled.
+// Dense GEMV stream kernel settings: lanes per row (g), prefetch depth d
+// (chunks in flight per lane), activations staged in LDS (xl), workgroups in
+// the grid (wgs; rows are dealt round-robin over its groups).  The compiled
+// (g, d) pairs are listed in MXQ_STREAM_SHAPES.
 struct GemvConfig {
-    int g, s, r;
+    int g, d, xl;
+    int64_t wgs;
 };
 
-#define MXQ_GEMV_CONFIGS(X) \
-    X(16, 1, 4)             \
-    X(16, 1, 2)             \
-    X(16, 1, 1)             \
-    X(16, 2, 1)             \
-    X(16, 4, 1)             \
-    X(16, 8, 1)             \
-    X(16, 16, 1)            \
-    X(8, 1, 1)              \
-    X(8, 1, 2)              \
-    X(4, 1, 1)
+#define MXQ_STREAM_SHAPES(X) X(16, 4) X(32, 4) X(64, 4) X(64, 8)
 
 struct MoeArgs {
     int fmt;

@@ -30,7 +30,7 @@ __device__ __forceinline__ void moe_batch(const uint8_t* codes, const uint8_t* s
         xs[b] = x + xrow * k;
         ys[b] = b < cnt ? y + (int64_t)q * n : nullptr;
     }
-    rows_core<FMT, CB, B, G, 1, R>(codes, scales, n, k, row0, xs, ys, gmul, nullptr);
+    rows_core<FMT, CB, B, G, 1, R, false>(codes, scales, n, k, row0, xs, ys, gmul, nullptr, nullptr);
 }
 
 template <int FMT, int CB, int G, int R>

