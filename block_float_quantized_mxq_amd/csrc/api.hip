@@ -72,31 +72,22 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 namespace mxq {
 
-// Dense GEMV stream settings: 64 lanes per row block (1 KB-contiguous loads)
-// when the row has at least 64 chunks, else 32 or 16; rows per group chosen so
-// that the grid holds about 432 workgroups (1.7 per CU) with a whole number of
-// blocks per group.  MXQ_GEMV_CONFIG="g,d,xl,wgs" overrides the choice (used
-// only to compare variants when tuning).
+// Dense GEMV kernel settings: chosen from the shape by the launcher unless
+// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu" overrides them (used only to compare
+// variants when tuning).
 GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
-    (void)batch;
-    if (const char* env = std::getenv("MXQ_GEMV_CONFIG")) {
-        int g = 0, d = 0, xl = 0;
-        long long wgs = 0;
-        if (std::sscanf(env, "%d,%d,%d,%lld", &g, &d, &xl, &wgs) == 4) return GemvConfig{g, d, xl, (int64_t)wgs};
+    (void)fmt, (void)n, (void)k, (void)batch;
+    GemvConfig c;
+    if (const char* env = std::getenv("MXQ_GEMV_ROWS")) {
+        int g = 0, s = 0, r = 0, occ = 0;
+        if (std::sscanf(env, "%d,%d,%d,%d", &g, &s, &r, &occ) == 4) {
+            c.rows_g = g;
+            c.rows_s = s;
+            c.rows_r = r;
+            c.rows_occ = occ;
+        }
     }
-    const int64_t cb = (code_bytes_per_row(fmt, k) % 16 == 0) ? 16 : 8;
-    const int64_t nchunks = code_bytes_per_row(fmt, k) / cb;
-    const int g = nchunks >= 64 ? 64 : (nchunks >= 32 ? 32 : 16);
-    int p = 0;
-    for (int cand : {1, 2, 4})
-        if (p == 0 && (cand * nchunks) % g == 0) p = cand;
-    if (p == 0) p = 1;
-    const int64_t per_wg = 256 / g;
-    const int64_t nblocks = (n + p - 1) / p;
-    int64_t bpg = (nblocks + 432 * per_wg / 2) / (432 * per_wg);  // blocks per group, rounded
-    if (bpg < 1) bpg = 1;
-    const int64_t wgs = (nblocks + bpg * per_wg - 1) / (bpg * per_wg);
-    return GemvConfig{g, 4, 1, wgs};
+    return c;
 }
 
 }  // namespace mxq

@@ -1,9 +1,8 @@
-// gemv_impl.hpp -- launcher of the dense GEMV stream kernel (gemv_stream.hpp)
-// for one format; each format is instantiated in its own translation unit
-// (gemv_<format>.hip) so the instances compile in parallel.
+// gemv_impl.hpp -- the dense GEMV kernel and its launcher for one format; each
+// format is instantiated in its own translation unit (gemv_<format>.hip) so
+// the instances compile in parallel.
 #pragma once
 
-#include "gemv_stream.hpp"
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
@@ -13,51 +12,12 @@ namespace mxq {
 // within the 160 KB of LDS).
 constexpr int64_t kMaxXLds = 72 * 1024;
 
-template <int FMT, int CB, int B, int G, int P, int D, bool XL>
-static void launch_stream_inst(const GemvArgs& a, int64_t wgs, hipStream_t st) {
-    const int64_t per_wg = kThreads / G;
-    const int64_t nblocks = (a.n + P - 1) / P;
-    const int64_t need = (nblocks + per_wg - 1) / per_wg;  // one block per group at most
-    const int64_t blocks = wgs < need ? wgs : need;
-    const size_t lds = XL ? (size_t)x_lds_bytes<FMT, CB>(a.k, B) : 0;
-    hipLaunchKernelGGL((gemv_stream_kernel<FMT, CB, B, G, P, D, XL>), dim3((unsigned)blocks), dim3(kThreads), lds, st,
-                       a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch);
-}
-
-// Rows per block for G lanes: the smallest P with P * nchunks a multiple of
-// G (0 if none of the compiled P values fits, or the row has fewer than G chunks).
-inline int stream_rows_per_block(int64_t nchunks, int g) {
-    if (nchunks < g) return 0;
-    for (int p : {1, 2, 4}) if ((p * nchunks) % g == 0) return p;
-    return 0;
-}
-
-template <int FMT, int CB, int B>
-static bool launch_gemv_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
-    if (!cfg.xl || x_lds_bytes<FMT, CB>(a.k, B) > kMaxXLds) return false;
-    const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
-    const int p = stream_rows_per_block(nchunks, cfg.g);
-    const int64_t wgs = cfg.wgs > 0 ? cfg.wgs : 1024;
-#define MXQ_STREAM_CASE(G_, D_)                                                           \
-    if (cfg.g == G_ && cfg.d == D_) {                                                    \
-        if (p == 1) launch_stream_inst<FMT, CB, B, G_, 1, D_, true>(a, wgs, st);         \
-        else if (p == 2) launch_stream_inst<FMT, CB, B, G_, 2, D_, true>(a, wgs, st);    \
-        else if (p == 4) launch_stream_inst<FMT, CB, B, G_, 4, D_, true>(a, wgs, st);    \
-        else return false;                                                               \
-        return true;                                                                     \
-    }
-    MXQ_STREAM_SHAPES(MXQ_STREAM_CASE)
-#undef MXQ_STREAM_CASE
-    return false;
-}
-
-// ---- fallback: row tiles through rows_core (any k, any batch) -------------
-//
-// Used when the stream kernel does not apply: activations too large for LDS
-// (long rows at batch > 1) or rows whose chunk count fits no block shape.
-// Persistent grid of row tiles; each tile is R rows per group of G lanes,
-// split S ways along k (partials combined through LDS), activations read from
-// LDS when they fit and otherwise from global memory, reused by the R rows.
+// Persistent grid of row tiles (rows_core.hpp): each tile is R rows per group
+// of G lanes, split S ways along k (partials combined through LDS); the
+// activations are read from LDS when they fit (staged once per workgroup)
+// and otherwise from global memory, each chunk reused by the R rows.  Tile
+// tile, tile + gridDim.x, ... go to one workgroup, so the GPU sweeps the
+// matrix front to back.
 template <int FMT, int CB, int B, int G, int S, int R, bool XL>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
@@ -81,12 +41,15 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
 }
 
 template <int FMT, int CB, int B, int G, int S, int R>
-static void launch_rows_inst(const GemvArgs& a, hipStream_t st) {
+static void launch_rows_inst(const GemvArgs& a, int64_t per_cu, hipStream_t st) {
     using T = RowTile<G, S, R>;
     const int64_t ntiles = (a.n + T::ROWS - 1) / T::ROWS;
     const bool xl = x_lds_bytes<FMT, CB>(a.k, B) <= kMaxXLds;
     const size_t lds = xl ? (size_t)x_lds_bytes<FMT, CB>(a.k, B) : 0;
-    const int64_t cap = xl && lds > 40 * 1024 ? 512 : 1024;  // stay resident: LDS is 160 KB per CU
+    // stay resident: no more workgroups than fit in 160 KB of LDS per CU
+    const int64_t fit = (160 * 1024) / ((int64_t)lds + 4096);
+    if (per_cu > fit) per_cu = fit > 0 ? fit : 1;
+    const int64_t cap = 256 * per_cu;
     const int64_t blocks = ntiles < cap ? ntiles : cap;
     if (xl)
         hipLaunchKernelGGL((gemv_rows_kernel<FMT, CB, B, G, S, R, true>), dim3((unsigned)blocks), dim3(kThreads), lds,
@@ -96,38 +59,48 @@ static void launch_rows_inst(const GemvArgs& a, hipStream_t st) {
                            st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles);
 }
 
+// Row-tile settings (lanes per row g, k split s, rows per lane r, workgroups
+// per CU) for a shape; rows_cfg.g == 0 selects them from the shape.
 template <int FMT, int CB, int B>
-static bool launch_rows_b(const GemvArgs& a, hipStream_t st) {
+static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
     const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
-    if (nchunks < 8) { launch_rows_inst<FMT, CB, B, 4, 1, 1>(a, st); return true; }
-    if (nchunks < 16) { launch_rows_inst<FMT, CB, B, 8, 1, 1>(a, st); return true; }
-    // rows per lane: reuse each activation chunk across 4 rows at batch > 1;
-    // split k until the grid has about 1024 tiles, keeping >= 2 chunks per lane
-    if (B == 1) {
-        if (a.n / 16 >= 1024 || nchunks < 64) launch_rows_inst<FMT, CB, B, 16, 1, 1>(a, st);
-        else if (a.n / 8 >= 1024 || nchunks < 128) launch_rows_inst<FMT, CB, B, 16, 2, 1>(a, st);
-        else if (a.n / 4 >= 1024 || nchunks < 256) launch_rows_inst<FMT, CB, B, 16, 4, 1>(a, st);
-        else launch_rows_inst<FMT, CB, B, 16, 8, 1>(a, st);
-    } else {
-        if (a.n / 64 >= 1024 || nchunks < 64) launch_rows_inst<FMT, CB, B, 16, 1, 4>(a, st);
-        else if (a.n / 32 >= 1024 || nchunks < 128) launch_rows_inst<FMT, CB, B, 16, 2, 4>(a, st);
-        else launch_rows_inst<FMT, CB, B, 16, 8, 4>(a, st);
+    int g = cfg.rows_g, sp = cfg.rows_s, r = cfg.rows_r;
+    const int64_t occ = cfg.rows_occ > 0 ? cfg.rows_occ : 8;
+    if (g == 0) {
+        if (nchunks < 8) { g = 4; sp = 1; r = 1; }
+        else if (nchunks < 16) { g = 8; sp = 1; r = 1; }
+        else {
+            // Measured on MI355X: about 5 chunks per lane per row pass is best;
+            // 4 rows per lane (each activation chunk reused 4 times) wins at
+            // batch > 1 and for very long rows.
+            g = 16;
+            r = (B > 1 || nchunks >= 512) ? 4 : 1;
+            sp = 1;
+            int64_t best = -1;
+            for (int cand : {1, 2, 4, 8}) {
+                const int64_t per_lane10 = 10 * nchunks / (16 * cand);  // chunks per lane, x10
+                const int64_t dist = per_lane10 > 50 ? per_lane10 - 50 : 50 - per_lane10;
+                if (best < 0 || dist < best) { best = dist; sp = cand; }
+            }
+            if (r == 4 && sp == 8 && a.n < 2048) r = 2;
+        }
     }
-    return true;
-}
-
-template <int FMT, int CB, int B>
-static bool launch_any_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
-    if (launch_gemv_b<FMT, CB, B>(a, cfg, st)) return true;
-    return launch_rows_b<FMT, CB, B>(a, st);
+#define MXQ_ROWS_CASE(G_, S_, R_)                                         \
+    if (g == G_ && sp == S_ && r == R_) {                                \
+        launch_rows_inst<FMT, CB, B, G_, S_, R_>(a, occ, st);            \
+        return true;                                                     \
+    }
+    MXQ_ROWS_SHAPES(MXQ_ROWS_CASE)
+#undef MXQ_ROWS_CASE
+    return false;
 }
 
 template <int FMT, int CB>
 static bool launch_gemv_cb(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
-    if (a.batch <= 1) return launch_any_b<FMT, CB, 1>(a, cfg, st);
-    if (a.batch <= 2) return launch_any_b<FMT, CB, 2>(a, cfg, st);
-    if (a.batch <= 4) return launch_any_b<FMT, CB, 4>(a, cfg, st);
-    return launch_any_b<FMT, CB, 8>(a, cfg, st);
+    if (a.batch <= 1) return launch_rows_b<FMT, CB, 1>(a, cfg, st);
+    if (a.batch <= 2) return launch_rows_b<FMT, CB, 2>(a, cfg, st);
+    if (a.batch <= 4) return launch_rows_b<FMT, CB, 4>(a, cfg, st);
+    return launch_rows_b<FMT, CB, 8>(a, cfg, st);
 }
 
 }  // namespace mxq

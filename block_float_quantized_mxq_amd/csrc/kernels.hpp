@@ -19,16 +19,21 @@ struct GemvArgs {
     int64_t n, k, batch;
 };
 
-// Dense GEMV stream kernel settings: lanes per row (g), prefetch depth d
-// (chunks in flight per lane), activations staged in LDS (xl), workgroups in
-// the grid (wgs; rows are dealt round-robin over its groups).  The compiled
-// (g, d) pairs are listed in MXQ_STREAM_SHAPES.
+// Dense GEMV settings: lanes per row (rows_g), k split (rows_s), rows per lane
+// (rows_r) and workgroups per CU (rows_occ); 0 = chosen from the shape.  The
+// compiled (g, s, r) combinations are listed in MXQ_ROWS_SHAPES.
 struct GemvConfig {
-    int g, d, xl;
-    int64_t wgs;
+    int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
 };
 
-#define MXQ_STREAM_SHAPES(X) X(16, 4) X(32, 4) X(64, 4) X(64, 8)
+#define MXQ_ROWS_SHAPES(X) \
+    X(4, 1, 1) X(8, 1, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 8, 1) X(16, 8, 2) X(16, 1, 4) X(16, 2, 4) \
+    X(16, 4, 4) X(16, 8, 4)
+
+#define MXQ_STREAM_SHAPES(X) X(16, 4) X(16, 6) X(32, 4) X(32, 6) X(64, 4)
+
+// Compiled MoE tile shapes (lanes per row, k split, rows per lane).
+#define MXQ_MOE_SHAPES(X) X(4, 1, 1) X(8, 1, 1) X(8, 2, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 1, 2) X(16, 2, 2)
 
 struct MoeArgs {
     int fmt;

@@ -43,10 +43,27 @@ struct ChunkShape {
     static constexpr int XSTRIDE = XQ * 16 + 16;                   // LDS bytes per staged activation chunk
 };
 
-// LDS bytes needed to stage x[B][k] for the XL variant.
-template <int FMT, int CB>
+// LDS layout of staged activations: per batch entry, chunks in groups of XG
+// (XG = 1 for the row-tile kernels), each group
+// followed by 16 bytes of padding, so that lanes reading the same slot of
+// different groups fall on distinct banks.
+template <int FMT, int CB, int XG>
+__host__ __device__ constexpr int64_t x_group_bytes() {
+    return (int64_t)XG * ChunkShape<FMT, CB>::XQ * 16 + 16;
+}
+template <int FMT, int CB, int XG>
+__host__ __device__ constexpr int64_t x_lds_offset(int64_t c) {
+    return (c / XG) * x_group_bytes<FMT, CB, XG>() + (c % XG) * ChunkShape<FMT, CB>::XQ * 16;
+}
+template <int FMT, int CB, int XG>
+__host__ __device__ constexpr int64_t x_batch_bytes(int64_t k) {
+    return ((code_bytes_per_row(FMT, k) / CB + XG - 1) / XG) * x_group_bytes<FMT, CB, XG>();
+}
+
+// LDS bytes needed to stage x[B][k].
+template <int FMT, int CB, int XG = 1>
 __host__ __device__ constexpr int64_t x_lds_bytes(int64_t k, int b) {
-    return (int64_t)b * (code_bytes_per_row(FMT, k) / CB) * ChunkShape<FMT, CB>::XSTRIDE;
+    return (int64_t)b * x_batch_bytes<FMT, CB, XG>(k);
 }
 
 // Weights are read exactly once per call: load them with the nontemporal hint
@@ -109,9 +126,9 @@ struct RowTile {
     static constexpr int ROWS = ROWSETS * R;  // rows per workgroup
 };
 
-// Copies x[B][k] into LDS (layout: batch-major, one XSTRIDE slot per chunk).
-// Every thread of the workgroup must call it; it ends with a barrier.
-template <int FMT, int CB, int B>
+// Copies x[B][k] into LDS (layout above).  Every thread of the workgroup must
+// call it; it ends with a barrier.
+template <int FMT, int CB, int B, int XG = 1>
 __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t k, uint8_t* xlds) {
     using CS = ChunkShape<FMT, CB>;
     const int64_t nchunks = code_bytes_per_row(FMT, k) / CB;
@@ -119,10 +136,10 @@ __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t 
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs[b]);
-        uint8_t* dst = xlds + (int64_t)b * nchunks * CS::XSTRIDE;
+        uint8_t* dst = xlds + (int64_t)b * x_batch_bytes<FMT, CB, XG>(k);
         for (int64_t t = threadIdx.x; t < pieces; t += kThreads) {
             const int64_t c = t / CS::XQ, q = t % CS::XQ;
-            *reinterpret_cast<u32x4_t*>(dst + c * CS::XSTRIDE + 16 * q) = src[t];
+            *reinterpret_cast<u32x4_t*>(dst + x_lds_offset<FMT, CB, XG>(c) + 16 * q) = src[t];
         }
     }
     __syncthreads();
@@ -173,7 +190,7 @@ __device__ __forceinline__ void rows_core(const uint8_t* __restrict__ codes, con
         uint32_t xw[B][CS::NP];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const uint8_t* xp = XL ? xlds + ((int64_t)b * nchunks + c) * CS::XSTRIDE
+            const uint8_t* xp = XL ? xlds + (int64_t)b * nchunks * CS::XSTRIDE + x_lds_offset<FMT, CB, 1>(c)
                                    : reinterpret_cast<const uint8_t*>(xs[b]) + c * (CS::KPC * 2);
 #pragma unroll
             for (int q = 0; q < CS::XQ; ++q) {
