@@ -346,7 +346,7 @@ def main():
         k1 = d["kern1"]["gate_up"]
         line["roofline"] = dict(bound="hbm", achieved=round(k1["gbs"], 1), peak=PEAK_HBM_GBS, unit="GB/s",
                                 frac=round(k1["gbs"] / PEAK_HBM_GBS, 4), traffic=stored_traffic(),
-                                kernel="gemv_stream_kernel, MXFP4 gate/up 51200x5120, batch 1",
+                                kernel="gemv_rows_kernel, MXFP4 gate/up 51200x5120, batch 1",
                                 algorithmic_bytes_per_launch=wbytes["gate_up"], us_per_launch=round(k1["us"], 3))
         line["kernels_b1"] = {w: {kk: round(v, 3) for kk, v in d["kern1"][w].items()} for w in order}
         line["kernels_b4"] = {w: {kk: round(v, 3) for kk, v in d["kern4"][w].items()} for w in order}

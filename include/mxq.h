@@ -131,10 +131,12 @@ mxq_status_t mxq_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, 
  *
  *   Y[m][i] = sum_k X[m][k] * W[i][k]
  *
- * W is decoded to bf16 tiles (exact for every weight whose value is a normal
- * bf16 or zero, which holds for E8M0 exponents in [3, 250] with any code) and
- * multiplied on the bf16 matrix cores with fp32 accumulation; the NVFP4
- * per-tensor scale multiplies the fp32 result.
+ * W is decoded to bf16 tiles and multiplied on the bf16 matrix cores with fp32
+ * accumulation; the NVFP4 per-tensor scale multiplies the fp32 result.  The
+ * decoded tile is exact whenever each weight is zero or a normal bf16: for
+ * any code that holds for E8M0 bytes in [2, 252] (MXFP4) and [10, 246]
+ * (MXFP8, whose smallest subnormal is 2^-9), and always for NVFP4 (q * s has
+ * at most 6 significant bits and lies in [2^-10, 2688]).
  *   x       bf16 [m][k]
  *   y       [m][n], fp32 (y_dtype MXQ_OUT_F32) or bf16 rounded to nearest even
  *           from the fp32 result (MXQ_OUT_BF16)
