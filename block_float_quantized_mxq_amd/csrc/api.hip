@@ -26,10 +26,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
-// Per-device result of the gfx950 check: 0 unknown, 1 ok, 2 not usable.
+// Per-device result of the gfx950 check: 0 unknown, 1 ok, 2 not usable; and
+// the device's compute-unit count.
 std::atomic<int> g_device_ok[64];
+std::atomic<int> g_device_cus[64];
 
-mxq_status_t check_device() {
+// gfx950 check of the current device; on success *cus is its compute-unit count.
+mxq_status_t check_device(int* cus) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
         (void)hipGetLastError();
@@ -44,9 +47,12 @@ mxq_status_t check_device() {
             return MXQ_E_DEVICE;
         }
         state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
         g_device_ok[dev].store(state, std::memory_order_release);
     }
-    return state == 1 ? MXQ_OK : MXQ_E_DEVICE;
+    if (state != 1) return MXQ_E_DEVICE;
+    *cus = g_device_cus[dev].load(std::memory_order_relaxed);
+    return MXQ_OK;
 }
 
 mxq_status_t check_weight(int fmt, const uint8_t* codes, const uint8_t* scales, const float* gscale) {
@@ -73,18 +79,19 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 namespace mxq {
 
 // Dense GEMV kernel settings: chosen from the shape by the launcher unless
-// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu" overrides them (used only to compare
-// variants when tuning).
+// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu[,grid]" overrides them (used only to
+// compare variants when tuning).
 GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
     (void)fmt, (void)n, (void)k, (void)batch;
     GemvConfig c;
     if (const char* env = std::getenv("MXQ_GEMV_ROWS")) {
-        int g = 0, s = 0, r = 0, occ = 0;
-        if (std::sscanf(env, "%d,%d,%d,%d", &g, &s, &r, &occ) == 4) {
+        int g = 0, s = 0, r = 0, occ = 0, grid = 0;
+        if (std::sscanf(env, "%d,%d,%d,%d,%d", &g, &s, &r, &occ, &grid) >= 4) {
             c.rows_g = g;
             c.rows_s = s;
             c.rows_r = r;
             c.rows_occ = occ;
+            c.rows_grid = grid;
         }
     }
     return c;
@@ -117,8 +124,9 @@ MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scal
     if ((st = check_k(fmt, k)) != MXQ_OK) return st;
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
     if (n > kMaxDim || k > kMaxDim || batch > MXQ_MAX_BATCH) return MXQ_E_UNSUPPORTED;
-    if ((st = check_device()) != MXQ_OK) return st;
-    const mxq::GemvArgs a{fmt, codes, scales, global_scale, x, y, n, k, batch};
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::GemvArgs a{fmt, codes, scales, global_scale, x, y, n, k, batch, cus};
     return launched(mxq::launch_gemv(a, mxq::choose_gemv_config(fmt, n, k, batch), as_stream(stream)));
 }
 
@@ -136,9 +144,10 @@ MXQ_API mxq_status_t mxq_moe_gemv(int fmt, const uint8_t* codes, const uint8_t* 
         return MXQ_E_ALIGN;
     if (n > kMaxDim || k > kMaxDim || num_experts > kMaxDim || tokens > MXQ_MAX_BATCH || topk > MXQ_MAX_TOPK)
         return MXQ_E_UNSUPPORTED;
-    if ((st = check_device()) != MXQ_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::MoeArgs a{fmt, codes, scales, global_scale, expert_ids, x, x_per_slot ? 1 : 0, y,
-                         num_experts, n, k, tokens, topk};
+                         num_experts, n, k, tokens, topk, cus};
     return launched(mxq::launch_moe(a, as_stream(stream)));
 }
 
@@ -152,7 +161,8 @@ MXQ_API mxq_status_t mxq_gemm(int fmt, const uint8_t* codes, const uint8_t* scal
     if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return MXQ_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
     if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return MXQ_E_UNSUPPORTED;
-    if ((st = check_device()) != MXQ_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::GemmArgs a{fmt, codes, scales, global_scale, x, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k};
     return launched(mxq::launch_gemm(a, as_stream(stream)));
 }
@@ -166,7 +176,8 @@ MXQ_API mxq_status_t mxq_dequant(int fmt, const uint8_t* codes, const uint8_t* s
     if ((st = check_k(fmt, k)) != MXQ_OK) return st;
     if (!aligned(codes, 16) || !aligned(w, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
     if (rows > kMaxDim || k > kMaxDim) return MXQ_E_UNSUPPORTED;
-    if ((st = check_device()) != MXQ_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::DequantArgs a{fmt, codes, scales, global_scale, w, rows, k};
     return launched(mxq::launch_dequant(a, as_stream(stream)));
 }

@@ -3,21 +3,24 @@
 // the instances compile in parallel.
 #pragma once
 
+#include <atomic>
+
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
 namespace mxq {
 
-// Largest LDS allocation for staged activations (keeps two workgroups per CU
-// within the 160 KB of LDS).
+// Largest LDS allocation for staged activations (x of the 25600-long rows
+// of a down projection still fits three workgroups per CU).
 constexpr int64_t kMaxXLds = 72 * 1024;
 
 // Persistent grid of row tiles (rows_core.hpp): each tile is R rows per group
 // of G lanes, split S ways along k (partials combined through LDS); the
 // activations are read from LDS when they fit (staged once per workgroup)
-// and otherwise from global memory, each chunk reused by the R rows.  Tile
-// tile, tile + gridDim.x, ... go to one workgroup, so the GPU sweeps the
-// matrix front to back.
+// and otherwise from global memory, each chunk reused by the R rows.  Tiles
+// tile, tile + gridDim.x, ... go to one workgroup as one stream of passes, so
+// the GPU sweeps the matrix front to back; the first pass is in flight while
+// the activations are staged.
 template <int FMT, int CB, int B, int G, int S, int R, bool XL>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
@@ -25,6 +28,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
                                                              const uint16_t* __restrict__ x, float* __restrict__ y,
                                                              int64_t n, int64_t k, int batch, int64_t ntiles) {
     using T = RowTile<G, S, R>;
+    using E = RowEngine<FMT, CB, B, G, S, R, XL>;
     __shared__ float red[S > 1 ? S * T::ROWSETS * R * B : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
     const uint16_t* xs[B];
@@ -34,29 +38,56 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
         xs[b] = x + (int64_t)(b < batch ? b : 0) * k;
         ys[b] = b < batch ? y + (int64_t)b * n : nullptr;
     }
+    const E eng(codes, scales, n, k);
+    const int64_t tile = blockIdx.x;  // < ntiles: the grid never exceeds the tile count
+    const int64_t count = (ntiles - tile + gridDim.x - 1) / gridDim.x;
+    typename E::Pass pre;
+    eng.load_first(eng.rows(tile * T::ROWS), pre);
     const float gmul = (FMT == kNVFP4) ? gscale[0] : 1.0f;
     if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x)
-        rows_core<FMT, CB, B, G, S, R, XL>(codes, scales, n, k, tile * T::ROWS, xs, ys, gmul, red, xlds);
+    eng.run(tile * T::ROWS, (int64_t)gridDim.x * T::ROWS, count, pre, xs, ys, gmul, red, xlds);
+}
+
+// Workgroups of `kernel` that fit on one CU with `lds` bytes of dynamic LDS
+// (registers, waves and LDS together).  `cache` holds the last answer as
+// (lds << 16) | count, per kernel instance.
+template <typename K>
+static int64_t resident_per_cu(K kernel, size_t lds, std::atomic<int64_t>& cache) {
+    const int64_t c = cache.load(std::memory_order_relaxed);
+    if (c >= 0 && (c >> 16) == (int64_t)lds) return c & 0xFFFF;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        nb = 1;
+    }
+    if (nb < 1) nb = 1;
+    cache.store(((int64_t)lds << 16) | nb, std::memory_order_relaxed);
+    return nb;
 }
 
 template <int FMT, int CB, int B, int G, int S, int R>
-static void launch_rows_inst(const GemvArgs& a, int64_t per_cu, hipStream_t st) {
+static void launch_rows_inst(const GemvArgs& a, int64_t per_cu, int grid_mode, hipStream_t st) {
     using T = RowTile<G, S, R>;
+    static std::atomic<int64_t> occ_cache[2] = {{-1}, {-1}};
     const int64_t ntiles = (a.n + T::ROWS - 1) / T::ROWS;
     const bool xl = x_lds_bytes<FMT, CB>(a.k, B) <= kMaxXLds;
     const size_t lds = xl ? (size_t)x_lds_bytes<FMT, CB>(a.k, B) : 0;
-    // stay resident: no more workgroups than fit in 160 KB of LDS per CU
-    const int64_t fit = (160 * 1024) / ((int64_t)lds + 4096);
-    if (per_cu > fit) per_cu = fit > 0 ? fit : 1;
-    const int64_t cap = 256 * per_cu;
-    const int64_t blocks = ntiles < cap ? ntiles : cap;
-    if (xl)
-        hipLaunchKernelGGL((gemv_rows_kernel<FMT, CB, B, G, S, R, true>), dim3((unsigned)blocks), dim3(kThreads), lds,
-                           st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles);
-    else
-        hipLaunchKernelGGL((gemv_rows_kernel<FMT, CB, B, G, S, R, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                           st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles);
+    const auto kernel = xl ? gemv_rows_kernel<FMT, CB, B, G, S, R, true> : gemv_rows_kernel<FMT, CB, B, G, S, R, false>;
+    // Stay resident: no more workgroups per CU than fit at once.
+    const int64_t fit = resident_per_cu(kernel, lds, occ_cache[xl ? 1 : 0]);
+    if (per_cu > fit) per_cu = fit;
+    // As many workgroups as are resident at once (measured: more bytes in
+    // flight beats handing every workgroup the same number of tiles).
+    const int64_t cap = (int64_t)a.cus * per_cu;
+    int64_t blocks = ntiles < cap ? ntiles : cap;
+    if (grid_mode == 1) {
+        const int64_t rounds = (ntiles + cap - 1) / cap;
+        blocks = (ntiles + rounds - 1) / rounds;
+    } else if (grid_mode == 2) {
+        blocks = ntiles;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), lds, st, a.codes, a.scales, a.gscale, a.x, a.y,
+                       a.n, a.k, (int)a.batch, ntiles);
 }
 
 // Row-tile settings (lanes per row g, k split s, rows per lane r, workgroups
@@ -71,10 +102,10 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
         else if (nchunks < 16) { g = 8; sp = 1; r = 1; }
         else {
             // Measured on MI355X: about 5 chunks per lane per row pass is best;
-            // 4 rows per lane (each activation chunk reused 4 times) wins at
-            // batch > 1 and for very long rows.
+            // 2 rows per lane, or 4 (each activation chunk reused 4 times) at
+            // batch > 1 for very long rows or very many rows.
             g = 16;
-            r = (B > 1 || nchunks >= 512) ? 4 : 1;
+            r = (B > 1 && (nchunks >= 512 || a.n >= 32768)) ? 4 : 2;
             sp = 1;
             int64_t best = -1;
             for (int cand : {1, 2, 4, 8}) {
@@ -83,11 +114,12 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
                 if (best < 0 || dist < best) { best = dist; sp = cand; }
             }
             if (r == 4 && sp == 8 && a.n < 2048) r = 2;
+            if (r == 2 && sp == 8 && a.n < 1024) r = 1;
         }
     }
 #define MXQ_ROWS_CASE(G_, S_, R_)                                         \
     if (g == G_ && sp == S_ && r == R_) {                                \
-        launch_rows_inst<FMT, CB, B, G_, S_, R_>(a, occ, st);            \
+        launch_rows_inst<FMT, CB, B, G_, S_, R_>(a, occ, cfg.rows_grid, st); \
         return true;                                                     \
     }
     MXQ_ROWS_SHAPES(MXQ_ROWS_CASE)

@@ -17,6 +17,7 @@ struct GemvArgs {
     const uint16_t* x;
     float* y;
     int64_t n, k, batch;
+    int cus;  // compute units of the device
 };
 
 // Dense GEMV settings: lanes per row (rows_g), k split (rows_s), rows per lane
@@ -24,13 +25,12 @@ struct GemvArgs {
 // compiled (g, s, r) combinations are listed in MXQ_ROWS_SHAPES.
 struct GemvConfig {
     int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
+    int rows_grid = 0;  // 0: min(tiles, resident); 1: equal tiles per workgroup; 2: one workgroup per tile
 };
 
 #define MXQ_ROWS_SHAPES(X) \
-    X(4, 1, 1) X(8, 1, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 8, 1) X(16, 8, 2) X(16, 1, 4) X(16, 2, 4) \
-    X(16, 4, 4) X(16, 8, 4)
-
-#define MXQ_STREAM_SHAPES(X) X(16, 4) X(16, 6) X(32, 4) X(32, 6) X(64, 4)
+    X(4, 1, 1) X(8, 1, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 8, 1) X(16, 1, 2) X(16, 2, 2) X(16, 4, 2) \
+    X(16, 8, 2) X(16, 1, 4) X(16, 2, 4) X(16, 4, 4) X(16, 8, 4)
 
 // Compiled MoE tile shapes (lanes per row, k split, rows per lane).
 #define MXQ_MOE_SHAPES(X) X(4, 1, 1) X(8, 1, 1) X(8, 2, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 1, 2) X(16, 2, 2)
@@ -45,6 +45,7 @@ struct MoeArgs {
     int x_per_slot;
     float* y;
     int64_t experts, n, k, tokens, topk;
+    int cus;  // compute units of the device
 };
 
 struct DequantArgs {

@@ -18,7 +18,9 @@
 
 namespace mxq {
 
-constexpr int kMaxPairs = 8 * 16;  // MXQ_MAX_BATCH * MXQ_MAX_TOPK
+// Routing positions per call (MXQ_MAX_BATCH * MXQ_MAX_TOPK): two ids per lane.
+constexpr int kMaxPairs = 8 * 16;
+static_assert(kMaxPairs <= 128, "the kernel holds two routing ids per lane");
 constexpr int64_t kMoeMaxXLds = 64 * 1024;
 
 // Pairs per round: at most one per token when a token's experts are distinct,
@@ -28,56 +30,47 @@ static int moe_round_cap(int64_t tokens) {
     return tokens <= 1 ? 1 : (tokens <= 2 ? 2 : (tokens <= 4 ? 4 : 8));
 }
 
-// One round: up to B pairs routed to the same expert, contracted with the
-// expert's row tile.  With XL their activations are first staged in LDS.
+// Takes the next routing position from the two 64-bit masks (positions 0..63
+// in m0, 64..127 in m1), lowest first; -1 when both are empty.
+__device__ __forceinline__ int next_position(uint64_t& m0, uint64_t& m1) {
+    if (m0) {
+        const int q = __builtin_ctzll(m0);
+        m0 &= m0 - 1;
+        return q;
+    }
+    if (m1) {
+        const int q = 64 + __builtin_ctzll(m1);
+        m1 &= m1 - 1;
+        return q;
+    }
+    return -1;
+}
+
+// One round: the B positions in q[0..B) (q < 0: unused slot) contracted with
+// the expert's row tile, with activations staged in LDS when XL.
 template <int FMT, int CB, int B, int G, int S, int R, bool XL>
-__device__ __forceinline__ void moe_batch(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
-                                          int64_t row0, const int* sel, int cnt, const uint16_t* x,
-                                          int x_per_slot, int64_t topk, float* y, float gmul, float* red,
-                                          uint8_t* xlds) {
+__device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                                          int64_t row0, const int (&q)[8], const uint16_t* x, int x_per_slot,
+                                          int64_t topk, float* y, float gmul, float* red, uint8_t* xlds,
+                                          RowPass<FMT, CB, R>& pre) {
     const uint16_t* xs[B];
     float* ys[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-        const int q = sel[b < cnt ? b : 0];
-        const int64_t xrow = x_per_slot ? (int64_t)q : (int64_t)q / topk;
+        const int qq = q[b] >= 0 ? q[b] : q[0];
+        const int64_t xrow = x_per_slot ? (int64_t)qq : (int64_t)qq / topk;
         xs[b] = x + xrow * k;
-        ys[b] = b < cnt ? y + (int64_t)q * n : nullptr;
+        ys[b] = q[b] >= 0 ? y + (int64_t)q[b] * n : nullptr;
     }
     if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
-    rows_core<FMT, CB, B, G, S, R, XL>(codes, scales, n, k, row0, xs, ys, gmul, red, xlds);
+    const RowEngine<FMT, CB, B, G, S, R, XL> eng(codes, scales, n, k);
+    eng.run(row0, 0, 1, pre, xs, ys, gmul, red, xlds);
 }
 
-// Shared setup of both MoE kernels: the routing ids go to LDS in parallel;
-// returns the expert of position p, or -1 when this workgroup has nothing to
-// do (an earlier position holds the same expert, or the id is invalid, in
-// which case the NaN rows are written here).  sel[0..nsel) lists every
-// position >= p routed to the same expert.
-template <int ROWS>
-__device__ __forceinline__ int moe_setup(const int32_t* __restrict__ ids, int pairs, int p, int64_t experts,
-                                         int64_t n, int64_t row0, float* __restrict__ y, int* sids, int* sel,
-                                         int* nsel) {
-    for (int t = threadIdx.x; t < pairs; t += kThreads) sids[t] = ids[t];
-    __syncthreads();
-    const int e = sids[p];
-    if (e < 0 || (int64_t)e >= experts) {
-        for (int t = threadIdx.x; t < ROWS; t += kThreads)
-            if (row0 + t < n) y[(int64_t)p * n + row0 + t] = __builtin_nanf("");
-        return -1;
-    }
-    for (int q = 0; q < p; ++q)
-        if (sids[q] == e) return -1;  // an earlier position streams this expert
-    if (threadIdx.x == 0) {
-        int c = 0;
-        for (int q = p; q < pairs; ++q)
-            if (sids[q] == e) sel[c++] = q;
-        *nsel = c;
-    }
-    __syncthreads();
-    return e;
-}
-
-// Row tiles through rows_core; grid (row tile, routing position p).
+// Row tiles through the streaming engine; grid (row tile, routing position p).
+// Every wave reads the routing ids itself (two per lane) and finds, with
+// ballots, whether an earlier position holds the same expert and which later
+// positions share it: no LDS and no barrier before the weight loads start.
 template <int FMT, int CB, int G, int S, int R, bool XL>
 __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
@@ -87,33 +80,52 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict
                                                        float* __restrict__ y, int64_t experts, int64_t n, int64_t k,
                                                        int pairs, int64_t topk, int round_cap) {
     using T = RowTile<G, S, R>;
-    __shared__ int sids[kMaxPairs];
-    __shared__ int sel[kMaxPairs];
-    __shared__ int nsel;
     __shared__ float red[S > 1 ? S * T::ROWSETS * R * 8 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
     const int p = blockIdx.y;
     const int64_t row0 = (int64_t)blockIdx.x * T::ROWS;
-    const int e = moe_setup<T::ROWS>(ids, pairs, p, experts, n, row0, y, sids, sel, &nsel);
-    if (e < 0) return;
-    const int total = nsel;
+    const int wl = threadIdx.x & 63;
+    const int v0 = wl < pairs ? ids[wl] : -1;
+    const int v1 = wl + 64 < pairs ? ids[wl + 64] : -1;
+    const int e = __shfl(p < 64 ? v0 : v1, p & 63, 64);
+    if (e < 0 || (int64_t)e >= experts) {
+        for (int t = threadIdx.x; t < T::ROWS; t += kThreads)
+            if (row0 + t < n) y[(int64_t)p * n + row0 + t] = __builtin_nanf("");
+        return;
+    }
+    const uint64_t below0 = p >= 64 ? ~0ull : ((1ull << p) - 1ull);
+    const uint64_t below1 = p >= 64 ? ((1ull << (p - 64)) - 1ull) : 0ull;
+    uint64_t m0 = __ballot(v0 == e), m1 = __ballot(v1 == e);
+    if ((m0 & below0) | (m1 & below1)) return;  // an earlier position streams this expert
+    m0 &= ~below0;
+    m1 &= ~below1;
     const int64_t rowbytes = code_bytes_per_row(FMT, k);
     const uint8_t* ecodes = codes + (int64_t)e * n * rowbytes;
     const uint8_t* escales = scales + (int64_t)e * n * (k / BlockSize<FMT>::value);
+    // Weights first: the first pass is in flight while the activations load.
+    const RowEngine<FMT, CB, 1, G, S, R, XL> geo(ecodes, escales, n, k);
+    RowPass<FMT, CB, R> pre;
+    geo.load_first(geo.rows(row0), pre);
     const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
-    for (int base = 0; base < total; base += round_cap) {
-        if (base > 0) __syncthreads();  // LDS of the previous round fully consumed
-        const int cnt = total - base < round_cap ? total - base : round_cap;
-        const int* s = sel + base;
-        // the LDS of a round is sized for round_cap vectors, and cnt <= round_cap
-        if (cnt == 1)
-            moe_batch<FMT, CB, 1, G, S, R, XL>(ecodes, escales, n, k, row0, s, cnt, x, x_per_slot, topk, y, gmul, red, xlds);
-        else if (cnt == 2)
-            moe_batch<FMT, CB, 2, G, S, R, XL>(ecodes, escales, n, k, row0, s, cnt, x, x_per_slot, topk, y, gmul, red, xlds);
-        else if (cnt <= 4)
-            moe_batch<FMT, CB, 4, G, S, R, XL>(ecodes, escales, n, k, row0, s, cnt, x, x_per_slot, topk, y, gmul, red, xlds);
+    bool first = true;
+    while (m0 | m1) {
+        int q[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) q[b] = b < round_cap ? next_position(m0, m1) : -1;
+        if (!first) {
+            lds_barrier();  // the previous round's activations are no longer read
+            geo.load_first(geo.rows(row0), pre);
+        }
+        first = false;
+        // the LDS of a round is sized for round_cap vectors
+        if (q[1] < 0)
+            moe_round<FMT, CB, 1, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
+        else if (q[2] < 0)
+            moe_round<FMT, CB, 2, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
+        else if (q[4] < 0)
+            moe_round<FMT, CB, 4, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
         else
-            moe_batch<FMT, CB, 8, G, S, R, XL>(ecodes, escales, n, k, row0, s, cnt, x, x_per_slot, topk, y, gmul, red, xlds);
+            moe_round<FMT, CB, 8, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
     }
 }
 

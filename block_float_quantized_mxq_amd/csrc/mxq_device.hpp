@@ -6,11 +6,12 @@
 // "MLxcel 0.8 release" post (and slide 12 of the Strix Halo talk): codes are
 // turned into 16-bit floats inside the kernel, exactly, and then multiplied
 // with the activations.  On gfx950 the conversion is one hardware instruction
-// per two codes (V_CVT_SCALEF32_PK_BF16_FP4 / _FP8 with a unit scale), which
-// replaces the pages' bit-placement trick: every E2M1 and every finite E4M3
-// value is exactly representable in bf16, so the conversion is exact.  The
-// block scale is applied once per block partial sum in fp32 instead of per
-// element.
+// per two codes (V_CVT_SCALEF32_PK_BF16_FP4 / _FP8), which replaces the pages'
+// bit-placement trick: every E2M1 and every finite E4M3 value is exactly
+// representable in bf16.  An E8M0 block scale is a power of two and goes into
+// the conversion's scale operand; an E4M3 block scale (NVFP4) has mantissa
+// bits, which that operand ignores, so it multiplies the block's fp32 partial
+// sum instead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,6 +58,31 @@ __device__ __forceinline__ void decode_dwords(const uint32_t (&c)[DW], uint32_t 
         }
     }
 }
+
+// Same with an E8M0 block scale applied by the conversion: `sexp` is an fp32
+// whose exponent field is the E8M0 byte (the conversion uses only the
+// exponent of its scale operand, so byte 0 means 2^-127 and byte 255 gives
+// NaN, as the format defines).  Each result is bf16(q * 2^(u-127)), exact
+// wherever that is a normal bf16.
+template <int FMT, int DW>
+__device__ __forceinline__ void decode_dwords_scaled(const uint32_t (&c)[DW], float sexp,
+                                                     uint32_t (&p)[(FMT == kMXFP8) ? 2 * DW : 4 * DW]) {
+#pragma unroll
+    for (int d = 0; d < DW; ++d) {
+        if constexpr (FMT == kMXFP8) {
+            p[2 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], sexp, false));
+            p[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[d], sexp, true));
+        } else {
+            p[4 * d + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], sexp, 0));
+            p[4 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], sexp, 1));
+            p[4 * d + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], sexp, 2));
+            p[4 * d + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[d], sexp, 3));
+        }
+    }
+}
+
+// E8M0 byte as the exponent field of an fp32 (the scale operand above).
+__device__ __forceinline__ float e8m0_exponent(uint32_t u) { return __builtin_bit_cast(float, (u & 0xFFu) << 23); }
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }

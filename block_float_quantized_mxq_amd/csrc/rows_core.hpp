@@ -11,17 +11,27 @@
 // lanes of a group are summed with DPP, and the S groups through LDS, in a
 // fixed order: results are bit-identical run to run.
 //
+// Pipelining: a lane's chunk loads for pass i+1 are issued before the
+// arithmetic of pass i, the first pass of a tile is issued before the
+// activations are staged (so the two memory latencies overlap), and the last
+// pass of a tile issues the first pass of the workgroup's next tile.  LDS is
+// synchronised with a barrier that waits for LDS operations only, so
+// outstanding weight loads stay in flight across it.
+//
 // Per 16-byte chunk: MXFP4 = one 32-element block (one E8M0 byte), MXFP8 = half
 // a 32-element block, NVFP4 = two 16-element blocks (two E4M3 bytes).  An
 // 8-byte chunk is used for NVFP4 rows whose byte length is not a multiple of 16.
-// The block scale multiplies the block's fp32 partial sum; NVFP4's per-tensor
-// scale multiplies the final sum.
+// MX block scales are powers of two and go into the scaled conversion itself
+// (the decoded bf16 value q * 2^(u-127) is exact wherever it is a normal bf16);
+// NVFP4's E4M3 block scale multiplies the 16-element block's fp32 partial sum,
+// and its per-tensor scale multiplies the final sum.
 //
 // Activations: each lane needs the activation chunk matching its code chunk
 // for every batch entry.  With XL the workgroup first copies x[B][k] into LDS
-// (one padded 16-byte slot after every chunk, so the 16 lanes of a group hit
-// distinct banks) and the loop reads it from there; otherwise the loop loads
-// it from global memory (L1/L2 resident), once per chunk for all R rows.
+// (unpadded; the 16-byte pieces of a chunk are XOR-swizzled so that 16 lanes
+// reading the same piece of 16 consecutive chunks hit distinct banks) and the
+// loop reads it from there; otherwise the loop loads it from global memory
+// (L1/L2 resident), once per chunk for all R rows.
 #pragma once
 
 #include "mxq_device.hpp"
@@ -39,31 +49,24 @@ struct ChunkShape {
     static constexpr int BS = BlockSize<FMT>::value;               // elements per scale block
     static constexpr int PPS = (BS / 2 < NP) ? BS / 2 : NP;        // pairs sharing one scale
     static constexpr int NSG = NP / PPS;                           // scales per chunk
-    static constexpr int XQ = KPC * 2 / 16;                        // 16-byte activation loads per chunk
-    static constexpr int XSTRIDE = XQ * 16 + 16;                   // LDS bytes per staged activation chunk
+    static constexpr int XQ = KPC * 2 / 16;                        // 16-byte activation pieces per chunk
 };
 
-// LDS layout of staged activations: per batch entry, chunks in groups of XG
-// (XG = 1 for the row-tile kernels), each group
-// followed by 16 bytes of padding, so that lanes reading the same slot of
-// different groups fall on distinct banks.
-template <int FMT, int CB, int XG>
-__host__ __device__ constexpr int64_t x_group_bytes() {
-    return (int64_t)XG * ChunkShape<FMT, CB>::XQ * 16 + 16;
-}
-template <int FMT, int CB, int XG>
-__host__ __device__ constexpr int64_t x_lds_offset(int64_t c) {
-    return (c / XG) * x_group_bytes<FMT, CB, XG>() + (c % XG) * ChunkShape<FMT, CB>::XQ * 16;
-}
-template <int FMT, int CB, int XG>
-__host__ __device__ constexpr int64_t x_batch_bytes(int64_t k) {
-    return ((code_bytes_per_row(FMT, k) / CB + XG - 1) / XG) * x_group_bytes<FMT, CB, XG>();
+// LDS layout of staged activations: batch entry b, chunk c, piece q (16 bytes)
+// sits at 16-byte slot (b * nchunks + c) * XQ + (q ^ x_swizzle(c)).  The 64
+// banks of 4 bytes span 16 slots.  With XQ = 4 the slot of lane l (chunk
+// c0 + l, c0 a multiple of 16) is 4*(l & 3) + (q ^ (l >> 2)) mod 16; with
+// XQ = 2 it is 2*(l & 7) + (q ^ (l >> 3)): distinct for the 16 lanes either
+// way, with no padding.
+template <int FMT, int CB>
+__host__ __device__ constexpr int x_swizzle(int64_t c) {
+    return ChunkShape<FMT, CB>::XQ == 4 ? (int)((c >> 2) & 3) : (ChunkShape<FMT, CB>::XQ == 2 ? (int)((c >> 3) & 1) : 0);
 }
 
-// LDS bytes needed to stage x[B][k].
-template <int FMT, int CB, int XG = 1>
+// LDS bytes needed to stage x[B][k] (bf16).
+template <int FMT, int CB>
 __host__ __device__ constexpr int64_t x_lds_bytes(int64_t k, int b) {
-    return (int64_t)b * x_batch_bytes<FMT, CB, XG>(k);
+    return (int64_t)b * k * 2;
 }
 
 // Weights are read exactly once per call: load them with the nontemporal hint
@@ -126,135 +129,281 @@ struct RowTile {
     static constexpr int ROWS = ROWSETS * R;  // rows per workgroup
 };
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only, so global loads that are still in flight are not drained (a plain
+// __syncthreads() waits for them too).  The asm is a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Copies x[B][k] into LDS (layout above).  Every thread of the workgroup must
 // call it; it ends with a barrier.
-template <int FMT, int CB, int B, int XG = 1>
+template <int FMT, int CB, int B>
 __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t k, uint8_t* xlds) {
     using CS = ChunkShape<FMT, CB>;
-    const int64_t nchunks = code_bytes_per_row(FMT, k) / CB;
-    const int64_t pieces = nchunks * CS::XQ;
+    constexpr int U = 8;  // pieces per thread in flight
+    const int64_t pieces = k * 2 / 16;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs[b]);
-        uint8_t* dst = xlds + (int64_t)b * x_batch_bytes<FMT, CB, XG>(k);
-        for (int64_t t = threadIdx.x; t < pieces; t += kThreads) {
-            const int64_t c = t / CS::XQ, q = t % CS::XQ;
-            *reinterpret_cast<u32x4_t*>(dst + x_lds_offset<FMT, CB, XG>(c) + 16 * q) = src[t];
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xlds) + (int64_t)b * pieces;
+        for (int64_t t0 = threadIdx.x; t0 < pieces; t0 += U * kThreads) {
+            u32x4_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t t = t0 + (int64_t)u * kThreads;
+                if (t < pieces) v[u] = src[t];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t t = t0 + (int64_t)u * kThreads;
+                if (t < pieces) {
+                    const int64_t c = t / CS::XQ;
+                    const int q = (int)(t % CS::XQ);
+                    dst[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v[u];
+                }
+            }
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
-// Computes ys[b][row] = gmul * sum_k W[row][k] * xs[b][k] for the ROWS rows
-// starting at row0 (rows >= n are neither read nor written; ys[b] == nullptr
-// skips batch entry b).  Every thread of the workgroup must call it.  `red`
-// is LDS scratch of S*ROWSETS*R*B floats (unused when S == 1); with XL the
-// activations must already be staged in `xlds` (stage_x).  The function may be
-// called repeatedly (one row tile after another) by the same workgroup.
+// The streaming engine for one workgroup: geometry of the lane's chunks and
+// the pipelined pass loop over row tiles.  Every thread of the workgroup must
+// take part in every call.
+// One pass of one lane: R code chunks and their scale bytes.
+template <int FMT, int CB, int R>
+struct RowPass {
+    uint32_t cw[R][ChunkShape<FMT, CB>::DW];
+    uint32_t sb[R][ChunkShape<FMT, CB>::NSG];
+};
+
+// Row pointers of one tile for one lane.
+template <int R>
+struct RowPtrs {
+    const uint8_t* c[R];
+    const uint8_t* s[R];
+};
+
 template <int FMT, int CB, int B, int G, int S, int R, bool XL>
-__device__ __forceinline__ void rows_core(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                          int64_t n, int64_t k, int64_t row0, const uint16_t* const (&xs)[B],
-                                          float* const (&ys)[B], float gmul, float* red, uint8_t* xlds) {
+struct RowEngine {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
-    const int tid = threadIdx.x;
-    const int lane = tid % G, gid = tid / G, rs = gid / S, sp = gid % S;
-    const int64_t rowbytes = code_bytes_per_row(FMT, k);
-    const int64_t sbytes = k / CS::BS;
-    const int64_t nchunks = rowbytes / CB;
+    using Pass = RowPass<FMT, CB, R>;
+    using Rows = RowPtrs<R>;
 
-    const uint8_t* crow[R];
-    const uint8_t* srow[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        int64_t r = row0 + (int64_t)rs * R + j;
-        r = r < n ? r : n - 1;
-        crow[j] = codes + r * rowbytes;
-        srow[j] = scales + r * sbytes;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int64_t n, rowbytes, sbytes, nchunks, step, c0, niter;
+    int lane, rs, sp;
+
+    __device__ __forceinline__ RowEngine(const uint8_t* codes_, const uint8_t* scales_, int64_t n_, int64_t k) {
+        codes = codes_;
+        scales = scales_;
+        n = n_;
+        const int tid = threadIdx.x;
+        lane = tid % G;
+        const int gid = tid / G;
+        rs = gid / S;
+        sp = gid % S;
+        rowbytes = code_bytes_per_row(FMT, k);
+        sbytes = k / CS::BS;
+        nchunks = rowbytes / CB;
+        step = (int64_t)S * G;
+        c0 = (int64_t)sp * G + lane;
+        niter = (nchunks + step - 1) / step;  // the same for every lane
     }
-    float acc[R][B];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[j][b] = 0.0f;
 
-#pragma unroll 2
-    for (int64_t c = (int64_t)sp * G + lane; c < nchunks; c += (int64_t)S * G) {
-        uint32_t cw[R][CS::DW];
-        float sc[R][CS::NSG];
+    // Rows past n read row n-1 (their results are not written).
+    __device__ __forceinline__ Rows rows(int64_t row0) const {
+        Rows p;
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            load_code_chunk<CB>(crow[j] + c * CB, cw[j]);
-            load_chunk_scales<FMT, CB>(srow[j], c, sc[j]);
+            int64_t r = row0 + (int64_t)rs * R + j;
+            r = r < n ? r : n - 1;
+            p.c[j] = codes + r * rowbytes;
+            p.s[j] = scales + r * sbytes;
         }
+        return p;
+    }
+
+    // Issues the loads of the lane's chunk cv (c0 + i*step in pass i).  In
+    // the last pass lanes past the row end read the row's last chunk again;
+    // `compute` drops that contribution.
+    __device__ __forceinline__ void load(const Rows& rp, int cv, Pass& p) const {
+        const int64_t c = cv < nchunks ? cv : nchunks - 1;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            load_code_chunk<CB>(rp.c[j] + c * CB, p.cw[j]);
+            load_scale_bytes<FMT, CB>(rp.s[j], c, p.sb[j]);
+        }
+    }
+
+    // Issues the loads of pass 0 of the tile with row pointers rp.
+    __device__ __forceinline__ void load_first(const Rows& rp, Pass& p) const { load(rp, (int)c0, p); }
+
+    // Arithmetic of the pass with chunk cv on its loaded chunks.
+    __device__ __forceinline__ void compute(const Pass& p, int cv, const uint16_t* const (&xs)[B],
+                                            const uint8_t* xlds, float (&acc)[R][B]) const {
+        const bool valid = cv < nchunks;
+        const int64_t c = valid ? cv : nchunks - 1;
         uint32_t xw[B][CS::NP];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const uint8_t* xp = XL ? xlds + (int64_t)b * nchunks * CS::XSTRIDE + x_lds_offset<FMT, CB, 1>(c)
-                                   : reinterpret_cast<const uint8_t*>(xs[b]) + c * (CS::KPC * 2);
+            const u32x4_t* xp = XL ? reinterpret_cast<const u32x4_t*>(xlds) + ((int64_t)b * nchunks + c) * CS::XQ
+                                   : reinterpret_cast<const u32x4_t*>(xs[b]) + c * CS::XQ;
+            const int swz = XL ? x_swizzle<FMT, CB>(c) : 0;
 #pragma unroll
             for (int q = 0; q < CS::XQ; ++q) {
-                u32x4_t v = *reinterpret_cast<const u32x4_t*>(xp + 16 * q);
+                const u32x4_t v = xp[q ^ swz];
                 xw[b][4 * q + 0] = v[0]; xw[b][4 * q + 1] = v[1]; xw[b][4 * q + 2] = v[2]; xw[b][4 * q + 3] = v[3];
             }
         }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             uint32_t wp[CS::NP];
-            decode_dwords<FMT, CS::DW>(cw[j], wp);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-#pragma unroll
-                for (int q = 0; q < CS::NSG; ++q) {
-                    float part = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < CS::PPS; ++t) part = dot2_bf16(wp[q * CS::PPS + t], xw[b][q * CS::PPS + t], part);
-                    acc[j][b] = __builtin_fmaf(part, sc[j][q], acc[j][b]);
-                }
-            }
-        }
-    }
-
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[j][b] = group_sum<G>(acc[j][b]);
-
-    if constexpr (S == 1) {
-        if (lane == 0) {
-#pragma unroll
-            for (int j = 0; j < R; ++j) {
-                const int64_t r = row0 + (int64_t)rs * R + j;
-                if (r < n) {
-#pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        if (ys[b]) ys[b][r] = acc[j][b] * gmul;
-                }
-            }
-        }
-    } else {
-        if (lane == 0) {
-#pragma unroll
-            for (int j = 0; j < R; ++j)
-#pragma unroll
-                for (int b = 0; b < B; ++b) red[((sp * T::ROWSETS + rs) * R + j) * B + b] = acc[j][b];
-        }
-        __syncthreads();
-        for (int t = tid; t < T::ROWSETS * R; t += kThreads) {
-            const int j = t % R, set = t / R;
-            const int64_t r = row0 + (int64_t)set * R + j;
-            if (r < n) {
+            if constexpr (FMT == kNVFP4) {
+                float sc[CS::NSG];
+                scale_values<FMT, CB>(p.sb[j], sc);
+                decode_dwords<FMT, CS::DW>(p.cw[j], wp);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    float v = red[(set * R + j) * B + b];
+                    float a = acc[j][b];
 #pragma unroll
-                    for (int s = 1; s < S; ++s) v += red[((s * T::ROWSETS + set) * R + j) * B + b];
-                    if (ys[b]) ys[b][r] = v * gmul;
+                    for (int q = 0; q < CS::NSG; ++q) {
+                        float part = 0.0f;
+#pragma unroll
+                        for (int t = 0; t < CS::PPS; ++t) part = dot2_bf16(wp[q * CS::PPS + t], xw[b][q * CS::PPS + t], part);
+                        a = __builtin_fmaf(part, sc[q], a);
+                    }
+                    acc[j][b] = valid ? a : acc[j][b];
+                }
+            } else {
+                decode_dwords_scaled<FMT, CS::DW>(p.cw[j], e8m0_exponent(p.sb[j][0]), wp);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    float a = acc[j][b];
+#pragma unroll
+                    for (int t = 0; t < CS::NP; ++t) a = dot2_bf16(wp[t], xw[b][t], a);
+                    acc[j][b] = valid ? a : acc[j][b];
                 }
             }
         }
-        __syncthreads();  // `red` is rewritten by the next tile
     }
-}
+
+    // Sum over the G lanes and the S groups of the tile at row0 and store
+    // ys[b][row] = gmul * sum (rows >= n are not written; ys[b] == nullptr
+    // skips entry b).
+    __device__ __forceinline__ void finish(int64_t row0, float (&acc)[R][B], float* const (&ys)[B], float gmul,
+                                           float* red) const {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[j][b] = group_sum<G>(acc[j][b]);
+
+        if constexpr (S == 1) {
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t r = row0 + (int64_t)rs * R + j;
+                    if (r < n) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b)
+                            if (ys[b]) ys[b][r] = acc[j][b] * gmul;
+                    }
+                }
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) red[((sp * T::ROWSETS + rs) * R + j) * B + b] = acc[j][b];
+            }
+            lds_barrier();
+            for (int t = threadIdx.x; t < T::ROWSETS * R; t += kThreads) {
+                const int j = t % R, set = t / R;
+                const int64_t r = row0 + (int64_t)set * R + j;
+                if (r < n) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        float v = red[(set * R + j) * B + b];
+#pragma unroll
+                        for (int s = 1; s < S; ++s) v += red[((s * T::ROWSETS + set) * R + j) * B + b];
+                        if (ys[b]) ys[b][r] = v * gmul;
+                    }
+                }
+            }
+            lds_barrier();  // `red` is rewritten by the next tile
+        }
+    }
+
+    // Streams `count` tiles at rows first, first + row_step, ... as one
+    // sequence of passes; `pre` holds pass 0 of the first tile on entry.
+    // Every pass's loads are issued one pass ahead of its arithmetic, across
+    // tile boundaries, and the load instructions sit outside any branch (so
+    // the compiler's wait counts stay exact and the next pass stays in
+    // flight).  Passes go in pairs with two register buffers (no copies
+    // between them); the last one or two passes are peeled so that nothing is
+    // loaded past the end.  With XL the activations must already be in
+    // `xlds` (stage_x); `red` is LDS scratch of S*ROWSETS*R*B floats (unused
+    // when S == 1).
+    __device__ __forceinline__ void run(int64_t first, int64_t row_step, int64_t count, Pass& pre,
+                                        const uint16_t* const (&xs)[B], float* const (&ys)[B], float gmul,
+                                        float* red, const uint8_t* xlds) const {
+        const int64_t total = count * niter;
+        // load cursor: tile tl, pass il, chunk cl, rows rl (starts at the second pass)
+        int64_t tl = 0, il = 0;
+        int cl = (int)c0;
+        Rows rl = rows(first);
+        auto advance_load = [&]() {
+            cl += (int)step;
+            if (++il == niter) {
+                il = 0;
+                cl = (int)c0;
+                ++tl;
+                if (tl < count) rl = rows(first + tl * row_step);
+            }
+        };
+        advance_load();
+        // compute cursor: tile tc, pass ic, chunk cc
+        int64_t tc = 0, ic = 0;
+        int cc = (int)c0;
+        float acc[R][B];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[j][b] = 0.0f;
+        auto arith = [&](const Pass& cur) {
+            compute(cur, cc, xs, xlds, acc);
+            cc += (int)step;
+            if (++ic == niter) {  // tile done: reduce and store
+                finish(first + tc * row_step, acc, ys, gmul, red);
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int b = 0; b < B; ++b) acc[j][b] = 0.0f;
+                ic = 0;
+                cc = (int)c0;
+                ++tc;
+            }
+        };
+        Pass other;
+        int64_t P = 0;
+        for (; P + 2 < total; P += 2) {
+            load(rl, cl, other);
+            advance_load();
+            arith(pre);
+            load(rl, cl, pre);
+            advance_load();
+            arith(other);
+        }
+        if (total - P == 2) {
+            load(rl, cl, other);
+            arith(pre);
+            arith(other);
+        } else {
+            arith(pre);
+        }
+    }
+};
 
 }  // namespace mxq
