@@ -69,8 +69,8 @@ __host__ __device__ constexpr int64_t x_lds_bytes(int64_t k, int b) {
     return (int64_t)b * k * 2;
 }
 
-// Weights are read exactly once per call: load them with the nontemporal hint
-// so they do not displace the activations from the caches.
+// Weight codes are read exactly once per call: load them with the nontemporal
+// hint so they do not displace the activations from the caches.
 template <int CB>
 __device__ __forceinline__ void load_code_chunk(const uint8_t* p, uint32_t (&c)[CB / 4]) {
     if constexpr (CB == 16) {
@@ -82,7 +82,10 @@ __device__ __forceinline__ void load_code_chunk(const uint8_t* p, uint32_t (&c)[
     }
 }
 
-__device__ __forceinline__ uint32_t load_scale_byte(const uint8_t* p) { return __builtin_nontemporal_load(p); }
+// Scale bytes are loaded without the hint: consecutive passes read the same
+// cache line (16 bytes of it at a time), so it must stay cached between them
+// (measured on MI355X: nontemporal scale loads re-fetch and cost ~5%).
+__device__ __forceinline__ uint32_t load_scale_byte(const uint8_t* p) { return *p; }
 
 // Raw scale bytes for the NSG scale groups of chunk c of one row.
 template <int FMT, int CB>
