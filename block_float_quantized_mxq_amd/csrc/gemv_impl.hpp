@@ -10,6 +10,13 @@
 
 namespace mxq {
 
+// Passes each lane keeps in flight ahead of its arithmetic: one is enough with
+// several waves per SIMD to switch between.
+#ifndef MXQ_GEMV_AHEAD
+#define MXQ_GEMV_AHEAD 1
+#endif
+constexpr int kGemvAhead = MXQ_GEMV_AHEAD;
+
 // Largest LDS allocation for staged activations (x of the 25600-long rows
 // of a down projection still fits three workgroups per CU).
 constexpr int64_t kMaxXLds = 72 * 1024;
@@ -41,11 +48,12 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
     const E eng(codes, scales, n, k);
     const int64_t tile = blockIdx.x;  // < ntiles: the grid never exceeds the tile count
     const int64_t count = (ntiles - tile + gridDim.x - 1) / gridDim.x;
-    typename E::Pass pre;
-    eng.load_first(eng.rows(tile * T::ROWS), pre);
+    typename E::Cursor cur = eng.cursor(tile * T::ROWS, (int64_t)gridDim.x * T::ROWS, count, xs[0]);
+    PassRing<typename E::Pass, kGemvAhead + 1> ring;
+    eng.template prime<kGemvAhead>(cur, ring);
     const float gmul = (FMT == kNVFP4) ? gscale[0] : 1.0f;
     if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
-    eng.run(tile * T::ROWS, (int64_t)gridDim.x * T::ROWS, count, pre, xs, ys, gmul, red, xlds);
+    eng.template run<kGemvAhead>(cur, ring, xs, ys, gmul, red, xlds);
 }
 
 // Workgroups of `kernel` that fit on one CU with `lds` bytes of dynamic LDS

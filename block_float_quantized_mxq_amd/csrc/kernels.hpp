@@ -33,7 +33,7 @@ struct GemvConfig {
     X(16, 8, 2) X(16, 1, 4) X(16, 2, 4) X(16, 4, 4) X(16, 8, 4)
 
 // Compiled MoE tile shapes (lanes per row, k split, rows per lane).
-#define MXQ_MOE_SHAPES(X) X(4, 1, 1) X(8, 1, 1) X(8, 2, 1) X(16, 1, 1) X(16, 2, 1) X(16, 4, 1) X(16, 1, 2) X(16, 2, 2)
+#define MXQ_MOE_SHAPES(X) X(4, 1, 1) X(8, 1, 1) X(16, 1, 1) X(16, 1, 2)
 
 struct MoeArgs {
     int fmt;

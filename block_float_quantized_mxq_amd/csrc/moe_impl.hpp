@@ -1,4 +1,6 @@
-// moe.hip -- expert-indexed MoE GEMV.
+// moe_impl.hpp -- expert-indexed MoE GEMV: the kernel and its launcher for
+// one format; each format is instantiated in its own translation unit
+// (moe_<format>.hip) so the instances compile in parallel.
 //
 // Each (token, slot) pair routed to expert e needs W[e] . x_ts.  The section
 // "Unified memory" of the "MLxcel 0.8 release" post (and slide 4 of the talk)
@@ -10,6 +12,8 @@
 // and runs them as one batch through the shared streaming loop.  Dedupe and
 // gather happen in-kernel, so there is no host synchronisation and no
 // scratch memory.  A position whose id is outside [0, E) gets NaN outputs.
+#pragma once
+
 #include <cstdio>
 #include <cstdlib>
 
@@ -22,6 +26,13 @@ namespace mxq {
 constexpr int kMaxPairs = 8 * 16;
 static_assert(kMaxPairs <= 128, "the kernel holds two routing ids per lane");
 constexpr int64_t kMoeMaxXLds = 64 * 1024;
+
+// Passes each lane keeps in flight ahead of its arithmetic (measured on
+// MI355X: more than one does not help even at one token).
+#ifndef MXQ_MOE_AHEAD
+#define MXQ_MOE_AHEAD 1
+#endif
+constexpr int kMoeAhead = MXQ_MOE_AHEAD;
 
 // Pairs per round: at most one per token when a token's experts are distinct,
 // so rounds of min(8, tokens) pairs (rounded up to 1, 2, 4, 8); repeated ids
@@ -47,12 +58,13 @@ __device__ __forceinline__ int next_position(uint64_t& m0, uint64_t& m1) {
 }
 
 // One round: the B positions in q[0..B) (q < 0: unused slot) contracted with
-// the expert's row tile, with activations staged in LDS when XL.
-template <int FMT, int CB, int B, int G, int S, int R, bool XL>
+// the expert's row tile, with activations staged in LDS when XL.  The ring
+// holds the tile's first passes on entry.
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, int D>
 __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                           int64_t row0, const int (&q)[8], const uint16_t* x, int x_per_slot,
                                           int64_t topk, float* y, float gmul, float* red, uint8_t* xlds,
-                                          RowPass<FMT, CB, R>& pre) {
+                                          RowCursor<R>& cur, PassRing<RowPass<FMT, CB, R>, D + 1>& ring) {
     const uint16_t* xs[B];
     float* ys[B];
 #pragma unroll
@@ -64,21 +76,21 @@ __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* s
     }
     if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
     const RowEngine<FMT, CB, B, G, S, R, XL> eng(codes, scales, n, k);
-    eng.run(row0, 0, 1, pre, xs, ys, gmul, red, xlds);
+    eng.template run<D>(cur, ring, xs, ys, gmul, red, xlds);
 }
 
 // Row tiles through the streaming engine; grid (row tile, routing position p).
 // Every wave reads the routing ids itself (two per lane) and finds, with
 // ballots, whether an earlier position holds the same expert and which later
 // positions share it: no LDS and no barrier before the weight loads start.
-template <int FMT, int CB, int G, int S, int R, bool XL>
+template <int FMT, int CB, int G, int S, int R, bool XL, int RC>
 __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gscale,
                                                        const int32_t* __restrict__ ids,
                                                        const uint16_t* __restrict__ x, int x_per_slot,
                                                        float* __restrict__ y, int64_t experts, int64_t n, int64_t k,
-                                                       int pairs, int64_t topk, int round_cap) {
+                                                       int pairs, int64_t topk) {
     using T = RowTile<G, S, R>;
     __shared__ float red[S > 1 ? S * T::ROWSETS * R * 8 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
@@ -102,48 +114,67 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict
     const int64_t rowbytes = code_bytes_per_row(FMT, k);
     const uint8_t* ecodes = codes + (int64_t)e * n * rowbytes;
     const uint8_t* escales = scales + (int64_t)e * n * (k / BlockSize<FMT>::value);
-    // Weights first: the first pass is in flight while the activations load.
-    const RowEngine<FMT, CB, 1, G, S, R, XL> geo(ecodes, escales, n, k);
-    RowPass<FMT, CB, R> pre;
-    geo.load_first(geo.rows(row0), pre);
+    // Weights first: the first passes are in flight while the activations load.
+    using Geo = RowEngine<FMT, CB, 1, G, S, R, XL>;
+    const Geo geo(ecodes, escales, n, k);
+    RowCursor<R> cur = geo.cursor(row0, 0, 1, x);
+    const RowCursor<R> start = cur;
+    PassRing<RowPass<FMT, CB, R>, kMoeAhead + 1> ring;
+    geo.template prime<kMoeAhead>(cur, ring);
     const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
     bool first = true;
     while (m0 | m1) {
         int q[8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) q[b] = b < round_cap ? next_position(m0, m1) : -1;
+        for (int b = 0; b < 8; ++b) q[b] = b < RC ? next_position(m0, m1) : -1;
         if (!first) {
             lds_barrier();  // the previous round's activations are no longer read
-            geo.load_first(geo.rows(row0), pre);
+            cur = start;
+            geo.template prime<kMoeAhead>(cur, ring);
         }
         first = false;
-        // the LDS of a round is sized for round_cap vectors
-        if (q[1] < 0)
-            moe_round<FMT, CB, 1, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
-        else if (q[2] < 0)
-            moe_round<FMT, CB, 2, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
-        else if (q[4] < 0)
-            moe_round<FMT, CB, 4, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
-        else
-            moe_round<FMT, CB, 8, G, S, R, XL>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, pre);
+        // at most RC pairs per round (the LDS is sized for RC vectors); only
+        // the batch sizes up to RC are compiled, so a one-token launch keeps
+        // the registers of a one-vector loop
+        if (RC == 1 || q[1] < 0) {
+            moe_round<FMT, CB, 1, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+        } else if constexpr (RC >= 2) {
+            if (RC == 2 || q[2] < 0) {
+                moe_round<FMT, CB, 2, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+            } else if constexpr (RC >= 4) {
+                if (RC == 4 || q[4] < 0)
+                    moe_round<FMT, CB, 4, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+                else
+                    moe_round<FMT, CB, 8, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+            }
+        }
     }
+}
+
+template <int FMT, int CB, int G, int S, int R, int RC>
+static void launch_moe_rc(const MoeArgs& a, hipStream_t st) {
+    using T = RowTile<G, S, R>;
+    const int64_t tiles = (a.n + T::ROWS - 1) / T::ROWS;
+    const int pairs = (int)(a.tokens * a.topk);
+    const int64_t lds = x_lds_bytes<FMT, CB>(a.k, RC);
+    if (lds <= kMoeMaxXLds)
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true, RC>), dim3((unsigned)tiles, (unsigned)pairs),
+                           dim3(kThreads), (size_t)lds, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
+                           a.experts, a.n, a.k, pairs, a.topk);
+    else
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false, RC>), dim3((unsigned)tiles, (unsigned)pairs),
+                           dim3(kThreads), 0, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
+                           a.experts, a.n, a.k, pairs, a.topk);
 }
 
 template <int FMT, int CB, int G, int S, int R>
 static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
-    using T = RowTile<G, S, R>;
-    const int64_t tiles = (a.n + T::ROWS - 1) / T::ROWS;
-    const int pairs = (int)(a.tokens * a.topk);
-    const int round_cap = moe_round_cap(a.tokens);
-    const int64_t lds = x_lds_bytes<FMT, CB>(a.k, round_cap);
-    if (lds <= kMoeMaxXLds)
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true>), dim3((unsigned)tiles, (unsigned)pairs), dim3(kThreads),
-                           (size_t)lds, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y, a.experts, a.n,
-                           a.k, pairs, a.topk, round_cap);
-    else
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false>), dim3((unsigned)tiles, (unsigned)pairs),
-                           dim3(kThreads), 0, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
-                           a.experts, a.n, a.k, pairs, a.topk, round_cap);
+    switch (moe_round_cap(a.tokens)) {
+        case 1: launch_moe_rc<FMT, CB, G, S, R, 1>(a, st); break;
+        case 2: launch_moe_rc<FMT, CB, G, S, R, 2>(a, st); break;
+        case 4: launch_moe_rc<FMT, CB, G, S, R, 4>(a, st); break;
+        default: launch_moe_rc<FMT, CB, G, S, R, 8>(a, st); break;
+    }
 }
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
@@ -167,16 +198,6 @@ static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     }
     MXQ_MOE_SHAPES(MXQ_MOE_CASE)
 #undef MXQ_MOE_CASE
-    return false;
-}
-
-bool launch_moe(const MoeArgs& a, hipStream_t st) {
-    const bool wide = (code_bytes_per_row(a.fmt, a.k) % 16) == 0;
-    switch (a.fmt) {
-        case kMXFP4: return launch_moe_cb<kMXFP4, 16>(a, st);
-        case kMXFP8: return launch_moe_cb<kMXFP8, 16>(a, st);
-        case kNVFP4: return wide ? launch_moe_cb<kNVFP4, 16>(a, st) : launch_moe_cb<kNVFP4, 8>(a, st);
-    }
     return false;
 }
 

@@ -34,6 +34,8 @@
 // (L1/L2 resident), once per chunk for all R rows.
 #pragma once
 
+#include <type_traits>
+
 #include "mxq_device.hpp"
 
 namespace mxq {
@@ -186,12 +188,50 @@ struct RowPtrs {
     const uint8_t* s[R];
 };
 
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 (compile-time indices).
+template <int I, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < E) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, E>(f);
+    }
+}
+
+// N pass buffers indexed at compile time only (an array indexed by a loop
+// counter would live in scratch memory until the loop is unrolled).
+template <class P, int N>
+struct PassRing {
+    P head;
+    PassRing<P, N - 1> tail;
+    template <int I>
+    __device__ __forceinline__ P& at() {
+        if constexpr (I == 0) return head;
+        else return tail.template at<I - 1>();
+    }
+};
+template <class P>
+struct PassRing<P, 0> {};
+
+// Where the next pass to be loaded lies: tile tl of `count` (rows first +
+// tl * row_step), pass il, chunk cl, row pointers rl.  Past the last pass it
+// points at the first activation vector (a pass reads at most k/2 code bytes
+// and k/16 scale bytes of it, both within its 2k bytes), so loads can be
+// issued unconditionally and then hit the cache.
+template <int R>
+struct RowCursor {
+    int64_t first, row_step, count, tl, il;
+    int cl;
+    RowPtrs<R> rl;
+    const uint8_t* dummy;
+};
+
 template <int FMT, int CB, int B, int G, int S, int R, bool XL>
 struct RowEngine {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
     using Pass = RowPass<FMT, CB, R>;
     using Rows = RowPtrs<R>;
+    using Cursor = RowCursor<R>;
 
     const uint8_t* codes;
     const uint8_t* scales;
@@ -215,9 +255,10 @@ struct RowEngine {
         niter = (nchunks + step - 1) / step;  // the same for every lane
     }
 
-    // Rows past n read row n-1 (their results are not written).
-    __device__ __forceinline__ Rows rows(int64_t row0) const {
-        Rows p;
+    // Row pointers of the tile at row0 (element by element: a copied
+    // aggregate can end up in scratch memory).  Rows past n read row n-1
+    // (their results are not written).
+    __device__ __forceinline__ void set_rows(Rows& p, int64_t row0) const {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             int64_t r = row0 + (int64_t)rs * R + j;
@@ -225,7 +266,6 @@ struct RowEngine {
             p.c[j] = codes + r * rowbytes;
             p.s[j] = scales + r * sbytes;
         }
-        return p;
     }
 
     // Issues the loads of the lane's chunk cv (c0 + i*step in pass i).  In
@@ -239,9 +279,6 @@ struct RowEngine {
             load_scale_bytes<FMT, CB>(rp.s[j], c, p.sb[j]);
         }
     }
-
-    // Issues the loads of pass 0 of the tile with row pointers rp.
-    __device__ __forceinline__ void load_first(const Rows& rp, Pass& p) const { load(rp, (int)c0, p); }
 
     // Arithmetic of the pass with chunk cv on its loaded chunks.
     __device__ __forceinline__ void compute(const Pass& p, int cv, const uint16_t* const (&xs)[B],
@@ -339,34 +376,58 @@ struct RowEngine {
         }
     }
 
-    // Streams `count` tiles at rows first, first + row_step, ... as one
-    // sequence of passes; `pre` holds pass 0 of the first tile on entry.
-    // Every pass's loads are issued one pass ahead of its arithmetic, across
-    // tile boundaries, and the load instructions sit outside any branch (so
-    // the compiler's wait counts stay exact and the next pass stays in
-    // flight).  Passes go in pairs with two register buffers (no copies
-    // between them); the last one or two passes are peeled so that nothing is
-    // loaded past the end.  With XL the activations must already be in
-    // `xlds` (stage_x); `red` is LDS scratch of S*ROWSETS*R*B floats (unused
-    // when S == 1).
-    __device__ __forceinline__ void run(int64_t first, int64_t row_step, int64_t count, Pass& pre,
-                                        const uint16_t* const (&xs)[B], float* const (&ys)[B], float gmul,
-                                        float* red, const uint8_t* xlds) const {
-        const int64_t total = count * niter;
-        // load cursor: tile tl, pass il, chunk cl, rows rl (starts at the second pass)
-        int64_t tl = 0, il = 0;
-        int cl = (int)c0;
-        Rows rl = rows(first);
-        auto advance_load = [&]() {
-            cl += (int)step;
-            if (++il == niter) {
-                il = 0;
-                cl = (int)c0;
-                ++tl;
-                if (tl < count) rl = rows(first + tl * row_step);
+    __device__ __forceinline__ Cursor cursor(int64_t first, int64_t row_step, int64_t count, const uint16_t* x0) const {
+        Cursor u;
+        u.first = first;
+        u.row_step = row_step;
+        u.count = count;
+        u.tl = 0;
+        u.il = 0;
+        u.cl = (int)c0;
+        set_rows(u.rl, first);
+        u.dummy = reinterpret_cast<const uint8_t*>(x0);
+        return u;
+    }
+
+    __device__ __forceinline__ void advance(Cursor& u) const {
+        u.cl += (int)step;
+        if (++u.il == niter) {
+            u.il = 0;
+            u.cl = (int)c0;
+            ++u.tl;
+            // every slot is assigned on every path (selects, not branches):
+            // a store merged across branches would put the pointers in scratch
+            const bool more = u.tl < u.count;
+            set_rows(u.rl, u.first + (more ? u.tl : 0) * u.row_step);
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                u.rl.c[j] = more ? u.rl.c[j] : u.dummy;
+                u.rl.s[j] = more ? u.rl.s[j] : u.dummy;
             }
-        };
-        advance_load();
+        }
+    }
+
+    // Issues the loads of passes 0 .. D-1 into ring buffers 0 .. D-1.
+    template <int D>
+    __device__ __forceinline__ void prime(Cursor& u, PassRing<Pass, D + 1>& ring) const {
+        static_for<0, D>([&](auto d) {
+            load(u.rl, u.cl, ring.template at<decltype(d)::value>());
+            advance(u);
+        });
+    }
+
+    // Streams the cursor's tiles as one sequence of passes, D passes ahead:
+    // the loads of pass p + D are issued before the arithmetic of pass p,
+    // across tile boundaries.  ring[0 .. D-1] must hold passes 0 .. D-1
+    // (prime).  The ring is indexed statically (groups of D+1 passes, no
+    // register copies) and no load sits inside a branch, so the compiler's
+    // wait counts stay exact and D passes stay in flight.  With XL the
+    // activations must already be in `xlds` (stage_x); `red` is LDS scratch
+    // of S*ROWSETS*R*B floats (unused when S == 1).
+    template <int D>
+    __device__ __forceinline__ void run(Cursor& u, PassRing<Pass, D + 1>& ring, const uint16_t* const (&xs)[B],
+                                        float* const (&ys)[B], float gmul, float* red, const uint8_t* xlds) const {
+        const int64_t total = u.count * niter;
         // compute cursor: tile tc, pass ic, chunk cc
         int64_t tc = 0, ic = 0;
         int cc = (int)c0;
@@ -379,7 +440,7 @@ struct RowEngine {
             compute(cur, cc, xs, xlds, acc);
             cc += (int)step;
             if (++ic == niter) {  // tile done: reduce and store
-                finish(first + tc * row_step, acc, ys, gmul, red);
+                finish(u.first + tc * u.row_step, acc, ys, gmul, red);
 #pragma unroll
                 for (int j = 0; j < R; ++j)
 #pragma unroll
@@ -389,23 +450,20 @@ struct RowEngine {
                 ++tc;
             }
         };
-        Pass other;
         int64_t P = 0;
-        for (; P + 2 < total; P += 2) {
-            load(rl, cl, other);
-            advance_load();
-            arith(pre);
-            load(rl, cl, pre);
-            advance_load();
-            arith(other);
+        for (; P + (D + 1) <= total; P += D + 1) {
+            static_for<0, D + 1>([&](auto w) {
+                constexpr int W = decltype(w)::value;
+                load(u.rl, u.cl, ring.template at<(W + D) % (D + 1)>());
+                advance(u);
+                arith(ring.template at<W>());
+            });
         }
-        if (total - P == 2) {
-            load(rl, cl, other);
-            arith(pre);
-            arith(other);
-        } else {
-            arith(pre);
-        }
+        // the last passes are already loaded
+        static_for<0, D>([&](auto w) {
+            constexpr int W = decltype(w)::value;
+            if (P + W < total) arith(ring.template at<W>());
+        });
     }
 };
 

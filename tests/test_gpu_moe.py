@@ -29,7 +29,7 @@ def check(case, what, ids=None):
 
 
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-@pytest.mark.parametrize("tokens", [1, 2, 4])
+@pytest.mark.parametrize("tokens", [1, 2, 3, 4, 5, 8])
 def test_moe_layer_all_outputs(which, tokens):
     """128 experts, top-8 distinct ids per token; every routed output row checked."""
     case = synth.moe_layer(which, tokens, seed=0)
@@ -69,6 +69,27 @@ def test_more_pairs_than_one_batch():
     ids = np.zeros((8, 2), dtype=np.int32)
     ids[:, 1] = np.arange(8) % 4
     check(case, "moe 9+ pairs on expert 0", ids)
+
+
+def test_many_rounds_on_one_expert():
+    """Two tokens (two pairs per round), all sixteen slots on one expert: eight rounds."""
+    sc, ss, sx, _, _ = synth.streams(66)
+    codes, scales, g = synth.weights(1, sc, ss, 64, 768, experts=4)
+    ids = np.full((2, 8), 3, dtype=np.int32)
+    x = synth.bf16_normal(sx, (2, 8, 768))
+    check(dict(fmt=1, codes=codes, scales=scales, g=g, ids=ids, x=x, x_per_slot=1, experts=4, n=64, k=768,
+               tokens=2, topk=8), "moe 16 pairs on expert 3, rounds of 2")
+
+
+def test_moe_activations_from_global_memory():
+    """Eight activation vectors of 8192 elements do not fit the LDS budget: the
+    kernel reads them from global memory."""
+    sc, ss, sx, si, _ = synth.streams(77)
+    codes, scales, g = synth.weights(1, sc, ss, 20, 8192, experts=4)
+    ids = synth.moe_ids(si, 5, 2, 4)
+    x = synth.bf16_normal(sx, (5, 2, 8192))
+    check(dict(fmt=1, codes=codes, scales=scales, g=g, ids=ids, x=x, x_per_slot=1, experts=4, n=20, k=8192,
+               tokens=5, topk=2), "moe k=8192 tokens=5 (x from global memory)")
 
 
 @pytest.mark.parametrize("n,k", [(33, 64), (100, 96), (5, 4096)])
