@@ -100,6 +100,13 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
+// ---- synchronisation ---------------------------------------------------------------
+
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
+// only, so global loads that are still in flight are not drained (a plain
+// __syncthreads() waits for them too).  The asm is a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---- arithmetic -------------------------------------------------------------------
 
 // c + a.lo*b.lo + a.hi*b.hi with bf16 inputs and fp32 accumulation.

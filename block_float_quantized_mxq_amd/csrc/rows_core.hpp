@@ -134,11 +134,6 @@ struct RowTile {
     static constexpr int ROWS = ROWSETS * R;  // rows per workgroup
 };
 
-// Workgroup barrier for LDS traffic: waits for this wave's LDS operations
-// only, so global loads that are still in flight are not drained (a plain
-// __syncthreads() waits for them too).  The asm is a compiler memory barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Copies x[B][k] into LDS (layout above).  Every thread of the workgroup must
 // call it; it ends with a barrier.
 template <int FMT, int CB, int B>
