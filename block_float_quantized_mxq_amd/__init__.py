@@ -50,7 +50,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_gemv.argtypes = [I, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_gemm.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, P]
         L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
-        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant):
+        L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
+        L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -157,6 +159,66 @@ def moe_gemv(fmt, codes, scales, expert_ids, x, x_per_slot, global_scale=None, o
     _check(lib().mxq_moe_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(expert_ids), _ptr(x),
                               1 if x_per_slot else 0, _ptr(out), experts, n, k, tokens, topk, _stream(stream)),
            "mxq_moe_gemv")
+    return out
+
+
+def moe_route(logits, topk, renorm=False, ids=None, weights=None, stream=None):
+    """Top-k softmax routing of float32 logits [tokens, experts] -> (int32 ids, float32 weights), [tokens, topk]."""
+    logits = _dev(logits, torch.float32, "logits")
+    if logits.dim() != 2:
+        raise ValueError("logits must be [tokens, experts]")
+    tokens, experts = logits.shape
+    if ids is None:
+        ids = torch.empty((tokens, topk), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((tokens, topk), dtype=torch.float32, device=logits.device)
+    ids = _dev(ids, torch.int32, "ids")
+    weights = _dev(weights, torch.float32, "weights")
+    if ids.numel() != tokens * topk or weights.numel() != tokens * topk:
+        raise ValueError("ids and weights must hold tokens * topk elements")
+    _check(lib().mxq_moe_route(_ptr(logits), _ptr(ids), _ptr(weights), tokens, experts, topk, 1 if renorm else 0,
+                               _stream(stream)), "mxq_moe_route")
+    return ids, weights
+
+
+def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights, x, gu_global_scale=None,
+              dn_global_scale=None, h=None, out=None, stream=None):
+    """MoE decode block -> float32 [tokens, hidden]: y[t] = sum_s w[t][s] * W_dn[e] . bf16(silu(gate) * up),
+    with gate/up = W_gu[e] . x[t] (rows [0, dff) and [dff, 2 dff) of the gate/up bank).
+    h is the float32 [tokens, topk, 2 dff] workspace (allocated when None)."""
+    gu_codes = _dev(gu_codes, torch.uint8, "gu_codes")
+    gu_scales = _dev(gu_scales, torch.uint8, "gu_scales")
+    dn_codes = _dev(dn_codes, torch.uint8, "dn_codes")
+    dn_scales = _dev(dn_scales, torch.uint8, "dn_scales")
+    expert_ids = _dev(expert_ids, torch.int32, "expert_ids")
+    weights = _dev(weights, torch.float32, "weights")
+    x = _dev(x, torch.bfloat16, "x")
+    gu_global_scale = _dev(gu_global_scale, torch.float32, "gu_global_scale")
+    dn_global_scale = _dev(dn_global_scale, torch.float32, "dn_global_scale")
+    experts, two_dff = gu_codes.shape[0], gu_codes.shape[1]
+    hidden = _check_weight(fmt, gu_codes, gu_scales, gu_global_scale, experts=experts)
+    dff = _check_weight(fmt, dn_codes, dn_scales, dn_global_scale, experts=experts)
+    if two_dff != 2 * dff or tuple(dn_codes.shape[:2]) != (experts, hidden):
+        raise ValueError(f"gate/up bank {tuple(gu_codes.shape)} and down bank {tuple(dn_codes.shape)} disagree")
+    if expert_ids.dim() != 2 or tuple(weights.shape) != tuple(expert_ids.shape):
+        raise ValueError("expert_ids and weights must both be [tokens, topk]")
+    tokens, topk = expert_ids.shape
+    if tuple(x.shape) != (tokens, hidden):
+        raise ValueError(f"x must have shape {(tokens, hidden)}, got {tuple(x.shape)}")
+    if h is None:
+        h = torch.empty((tokens, topk, 2 * dff), dtype=torch.float32, device=gu_codes.device)
+    h = _dev(h, torch.float32, "h")
+    if h.numel() < tokens * topk * 2 * dff:
+        raise ValueError("h must hold tokens * topk * 2 * dff elements")
+    if out is None:
+        out = torch.empty((tokens, hidden), dtype=torch.float32, device=gu_codes.device)
+    out = _dev(out, torch.float32, "out")
+    if out.numel() != tokens * hidden:
+        raise ValueError("out must hold tokens * hidden elements")
+    _check(lib().mxq_moe_block(fmt, _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global_scale), _ptr(dn_codes),
+                               _ptr(dn_scales), _ptr(dn_global_scale), _ptr(expert_ids), _ptr(weights), _ptr(x),
+                               _ptr(h), _ptr(out), experts, hidden, dff, tokens, topk, _stream(stream)),
+           "mxq_moe_block")
     return out
 
 

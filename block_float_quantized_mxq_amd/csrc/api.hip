@@ -113,7 +113,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 1; }
+MXQ_API int mxq_abi_version(void) { return 2; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -180,4 +180,46 @@ MXQ_API mxq_status_t mxq_dequant(int fmt, const uint8_t* codes, const uint8_t* s
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::DequantArgs a{fmt, codes, scales, global_scale, w, rows, k};
     return launched(mxq::launch_dequant(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_moe_route(const float* logits, int32_t* expert_ids, float* weights, int64_t tokens,
+                                   int64_t num_experts, int64_t topk, int renorm, void* stream) {
+    if (!logits || !expert_ids || !weights) return MXQ_E_NULLPTR;
+    if (tokens <= 0 || num_experts <= 0 || topk <= 0 || topk > num_experts) return MXQ_E_SHAPE;
+    if (!aligned(logits, 4) || !aligned(expert_ids, 4) || !aligned(weights, 4)) return MXQ_E_ALIGN;
+    if (tokens > MXQ_MAX_BATCH || topk > MXQ_MAX_TOPK || num_experts > 1024) return MXQ_E_UNSUPPORTED;
+    mxq_status_t st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::RouteArgs a{logits, expert_ids, weights, tokens, num_experts, topk, renorm ? 1 : 0};
+    return launched(mxq::launch_moe_route(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
+                                   const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
+                                   const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h,
+                                   float* y, int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens,
+                                   int64_t topk, void* stream) {
+    mxq_status_t st = check_weight(fmt, gu_codes, gu_scales, gu_gscale);
+    if (st != MXQ_OK) return st;
+    if ((st = check_weight(fmt, dn_codes, dn_scales, dn_gscale)) != MXQ_OK) return st;
+    if (!expert_ids || !weights || !x || !h || !y) return MXQ_E_NULLPTR;
+    if (num_experts <= 0 || tokens <= 0 || topk <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, hidden)) != MXQ_OK) return st;
+    if ((st = check_k(fmt, dff)) != MXQ_OK) return st;
+    if (!aligned(gu_codes, 16) || !aligned(dn_codes, 16) || !aligned(x, 16) || !aligned(h, 16) || !aligned(y, 4) ||
+        !aligned(expert_ids, 4) || !aligned(weights, 4) || !aligned(gu_gscale, 4) || !aligned(dn_gscale, 4))
+        return MXQ_E_ALIGN;
+    if (hidden > kMaxDim || dff > kMaxDim || num_experts > kMaxDim || tokens > MXQ_MAX_BATCH || topk > MXQ_MAX_TOPK)
+        return MXQ_E_UNSUPPORTED;
+    const int64_t slots = topk <= 1 ? 1 : topk <= 2 ? 2 : topk <= 4 ? 4 : topk <= 8 ? 8 : 16;
+    if (slots * dff * 2 > mxq::kMoeBlockMaxLds) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::MoeArgs gu{fmt, gu_codes, gu_scales, gu_gscale, expert_ids, x, 0, h, num_experts, 2 * dff, hidden,
+                          tokens, topk, cus};
+    if ((st = launched(mxq::launch_moe(gu, as_stream(stream)))) != MXQ_OK) return st;
+    const mxq::MoeBlockArgs dn{fmt, dn_codes, dn_scales, dn_gscale, expert_ids, weights, h, y, num_experts, hidden, dff,
+                               tokens, topk};
+    return launched(mxq::launch_moe_down(dn, as_stream(stream)));
 }

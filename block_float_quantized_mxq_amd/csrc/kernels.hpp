@@ -71,6 +71,33 @@ struct GemmArgs {
 GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch);
 bool launch_gemv(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st);
 bool launch_moe(const MoeArgs& a, hipStream_t st);
+
+struct RouteArgs {
+    const float* logits;
+    int32_t* ids;
+    float* weights;
+    int64_t tokens, experts, topk;
+    int renorm;
+};
+
+struct MoeBlockArgs {
+    int fmt;
+    const uint8_t* dn_codes;
+    const uint8_t* dn_scales;
+    const float* dn_gscale;
+    const int32_t* ids;
+    const float* weights;
+    const float* h;  // gate/up outputs [tokens][topk][2 dff]
+    float* y;        // [tokens][hidden]
+    int64_t experts, hidden, dff, tokens, topk;
+};
+
+// LDS budget of the down kernel's staged activations (slots rounded up to a
+// power of two, dff bf16 each).
+constexpr int64_t kMoeBlockMaxLds = 64 * 1024;
+
+bool launch_moe_route(const RouteArgs& a, hipStream_t st);
+bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st);
 bool launch_dequant(const DequantArgs& a, hipStream_t st);
 bool launch_gemm(const GemmArgs& a, hipStream_t st);
 

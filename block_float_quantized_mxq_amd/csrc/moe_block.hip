@@ -1,0 +1,220 @@
+// moe_block.hip -- the MoE decode block around the expert-indexed GEMV:
+// routing (softmax top-k over router logits) and the down projection that
+// consumes the gate/up outputs through SwiGLU and combines a token's routed
+// experts with their routing weights.
+//
+// The "affine MoE" row of the ROCm status table in the "Build from source"
+// manual runs single-token MoE decode as a fused two-kernel path, gate-up then
+// down; slide 13 of the talk lists that port.  Here the two kernels are the
+// expert-indexed gate/up GEMV (moe_impl.hpp, every routed expert read once)
+// and moe_down_kernel below:
+//
+//  * grid (row tile of the hidden dimension, token); a workgroup first turns
+//    the token's gate/up outputs into its topk bf16 activation vectors
+//    a_s = bf16(silu(gate) * up) in LDS (rounded to nearest even once), then
+//    streams, for each of its output rows, the rows of the topk routed down
+//    matrices: group s of each row set reads expert ids[t][s] (the streaming
+//    engine's per-slot mode) and the groups' sums are combined with the
+//    routing weights in a fixed order -- no atomics, bit-reproducible.
+//  * a token with an expert id outside [0, E) gets NaN outputs.
+//
+// Routing: one wave per token.  Selection compares the fp32 logits themselves
+// (larger first, equal logits: lower index first), so it does not depend on
+// how the softmax is rounded; the weights are the softmax probabilities of the
+// selected experts, optionally renormalised over them.
+#include <cstdlib>
+
+#include "kernels.hpp"
+#include "rows_core.hpp"
+
+namespace mxq {
+
+// ---- routing ---------------------------------------------------------------------
+
+// Largest (value, index) pair of the wave, equal values: lower index.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(v, off, 64);
+        const int oi = __shfl_xor(i, off, 64);
+        if (ov > v || (ov == v && oi < i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// One wave per token; lane l owns experts l, l + 64, ... (at most kRouteMaxPerLane).
+constexpr int kRouteMaxPerLane = 16;  // experts <= 1024
+
+__global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int64_t experts, int topk,
+                                                       int renorm, int32_t* __restrict__ ids,
+                                                       float* __restrict__ weights) {
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* l = logits + t * experts;
+    float v[kRouteMaxPerLane];
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+        const int64_t e = (int64_t)i * 64 + lane;
+        v[i] = e < experts ? l[e] : -__builtin_huge_valf();
+        mx = v[i] > mx ? v[i] : mx;
+    }
+    int dummy = 0;
+    wave_argmax(mx, dummy);
+    float den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i)
+        if ((int64_t)i * 64 + lane < experts) den += expf(v[i] - mx);
+    den = wave_sum(den);
+    uint32_t taken = 0u;  // bit i: expert i*64 + lane already selected
+    float sel = 0.0f, wsel = 0.0f;
+    for (int s = 0; s < topk; ++s) {
+        float bv = -__builtin_huge_valf();
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kRouteMaxPerLane; ++i) {
+            const int64_t e = (int64_t)i * 64 + lane;
+            if (e < experts && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7FFFFFFF)) {
+                bv = v[i];
+                bi = (int)e;
+            }
+        }
+        wave_argmax(bv, bi);
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        const float p = expf(bv - mx) / den;
+        sel += p;
+        if (lane == s) wsel = p;
+        if (lane == 0) ids[t * topk + s] = bi;
+    }
+    if (lane < topk) weights[t * topk + lane] = renorm ? wsel / sel : wsel;
+}
+
+bool launch_moe_route(const RouteArgs& a, hipStream_t st) {
+    if (a.experts > 64 * kRouteMaxPerLane) return false;
+    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)a.tokens), dim3(64), 0, st, a.logits, a.experts, (int)a.topk,
+                       a.renorm, a.ids, a.weights);
+    return true;
+}
+
+// ---- down projection with SwiGLU input and weighted combine ---------------------------
+
+// a = bf16(silu(g) * u), computed in fp32 and rounded to nearest even once.
+__device__ __forceinline__ uint32_t swiglu_bf16x2(float g0, float u0, float g1, float u1) {
+    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
+    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
+    const bf16x2_t b = {(__bf16)a0, (__bf16)a1};
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+template <int FMT, int CB, int G, int S, int R>
+__global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ gscale,
+                                                            const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ weights,
+                                                            const float* __restrict__ h, float* __restrict__ y,
+                                                            int64_t experts, int64_t hidden, int64_t dff, int topk) {
+    using T = RowTile<G, S, R>;
+    using E = RowEngine<FMT, CB, 1, G, S, R, true, true>;
+    using CS = ChunkShape<FMT, CB>;
+    __shared__ float red[S > 1 ? S * T::ROWSETS * R : 1];
+    extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+    const int64_t t = blockIdx.y;
+    const int64_t row0 = (int64_t)blockIdx.x * T::ROWS;
+
+    // routing of token t: multipliers (weight times the NVFP4 tensor scale)
+    float smul[S];
+    bool ok = true;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        smul[s] = 0.0f;
+        if (s < topk) {
+            const int e = ids[t * topk + s];
+            ok = ok && e >= 0 && (int64_t)e < experts;
+            const float gs = (FMT == kNVFP4 && e >= 0 && (int64_t)e < experts) ? gscale[e] : 1.0f;
+            smul[s] = weights[t * topk + s] * gs;
+        }
+    }
+    if (!ok) {
+        for (int r = threadIdx.x; r < T::ROWS; r += kThreads)
+            if (row0 + r < hidden) y[t * hidden + row0 + r] = __builtin_nanf("");
+        return;
+    }
+    // this lane's group streams the down matrix of slot sp (slots past topk
+    // repeat slot 0 and are left out of the combine)
+    const int sp = (threadIdx.x / G) % S;
+    const int e = ids[t * topk + (sp < topk ? sp : 0)];
+    const int64_t rowbytes = code_bytes_per_row(FMT, dff);
+    const E eng(codes + (int64_t)e * hidden * rowbytes, scales + (int64_t)e * hidden * (dff / CS::BS), hidden, dff);
+    const uint16_t* xs[1] = {reinterpret_cast<const uint16_t*>(h)};
+    float* ys[1] = {y + t * hidden};
+    RowCursor<R> cur = eng.cursor(row0, 0, 1, xs[0]);
+    PassRing<RowPass<FMT, CB, R>, 2> ring;
+    eng.template prime<1>(cur, ring);  // weights first: in flight while the activations are built
+
+    // activations of the token's slots, slot s at elements s*dff .. of the staged block
+    const int64_t pieces = (int64_t)topk * dff / 8;
+    for (int64_t p = threadIdx.x; p < pieces; p += kThreads) {
+        const int64_t s = p * 8 / dff, j = p * 8 % dff;
+        const float* hg = h + (t * topk + s) * 2 * dff + j;
+        const float* hu = hg + dff;
+        const float4 g0 = *reinterpret_cast<const float4*>(hg), g1 = *reinterpret_cast<const float4*>(hg + 4);
+        const float4 u0 = *reinterpret_cast<const float4*>(hu), u1 = *reinterpret_cast<const float4*>(hu + 4);
+        const u32x4_t v = {swiglu_bf16x2(g0.x, u0.x, g0.y, u0.y), swiglu_bf16x2(g0.z, u0.z, g0.w, u0.w),
+                           swiglu_bf16x2(g1.x, u1.x, g1.y, u1.y), swiglu_bf16x2(g1.z, u1.z, g1.w, u1.w)};
+        const int64_t c = p / CS::XQ;
+        const int q = (int)(p % CS::XQ);
+        reinterpret_cast<u32x4_t*>(xlds)[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v;
+    }
+    lds_barrier();
+    eng.template run<1>(cur, ring, xs, ys, 1.0f, red, xlds, smul, topk);
+}
+
+template <int FMT, int CB, int G, int S>
+static void launch_down_inst(const MoeBlockArgs& a, hipStream_t st) {
+    using T = RowTile<G, S, 2>;
+    const int64_t tiles = (a.hidden + T::ROWS - 1) / T::ROWS;
+    const size_t lds = (size_t)S * a.dff * 2;
+    hipLaunchKernelGGL((moe_down_kernel<FMT, CB, G, S, 2>), dim3((unsigned)tiles, (unsigned)a.tokens), dim3(kThreads),
+                       lds, st, a.dn_codes, a.dn_scales, a.dn_gscale, a.ids, a.weights, a.h, a.y, a.experts, a.hidden,
+                       a.dff, (int)a.topk);
+}
+
+// Slots rounded up to a power of two; 8 lanes per row while a slot's row has
+// at most 32 chunks, else 16.
+template <int FMT, int CB>
+static bool launch_down_cb(const MoeBlockArgs& a, hipStream_t st) {
+    const int64_t chunks = code_bytes_per_row(FMT, a.dff) / CB;
+    const bool narrow = chunks <= 32;
+    switch (a.topk <= 1 ? 1 : a.topk <= 2 ? 2 : a.topk <= 4 ? 4 : a.topk <= 8 ? 8 : 16) {
+        case 1: narrow ? launch_down_inst<FMT, CB, 8, 1>(a, st) : launch_down_inst<FMT, CB, 16, 1>(a, st); return true;
+        case 2: narrow ? launch_down_inst<FMT, CB, 8, 2>(a, st) : launch_down_inst<FMT, CB, 16, 2>(a, st); return true;
+        case 4: narrow ? launch_down_inst<FMT, CB, 8, 4>(a, st) : launch_down_inst<FMT, CB, 16, 4>(a, st); return true;
+        case 8: narrow ? launch_down_inst<FMT, CB, 8, 8>(a, st) : launch_down_inst<FMT, CB, 16, 8>(a, st); return true;
+        default: narrow ? launch_down_inst<FMT, CB, 8, 16>(a, st) : launch_down_inst<FMT, CB, 16, 16>(a, st); return true;
+    }
+}
+
+bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st) {
+    // the staged activations of the padded slot count must fit the LDS budget
+    const int64_t slots = a.topk <= 1 ? 1 : a.topk <= 2 ? 2 : a.topk <= 4 ? 4 : a.topk <= 8 ? 8 : 16;
+    if (slots * a.dff * 2 > kMoeBlockMaxLds) return false;
+    switch (a.fmt) {
+        case kMXFP4: return launch_down_cb<kMXFP4, 16>(a, st);
+        case kMXFP8: return launch_down_cb<kMXFP8, 16>(a, st);
+        case kNVFP4:
+            return (code_bytes_per_row(kNVFP4, a.dff) % 16) == 0 ? launch_down_cb<kNVFP4, 16>(a, st)
+                                                                 : launch_down_cb<kNVFP4, 8>(a, st);
+    }
+    return false;
+}
+
+}  // namespace mxq

@@ -54,12 +54,13 @@ struct ChunkShape {
     static constexpr int XQ = KPC * 2 / 16;                        // 16-byte activation pieces per chunk
 };
 
-// LDS layout of staged activations: batch entry b, chunk c, piece q (16 bytes)
-// sits at 16-byte slot (b * nchunks + c) * XQ + (q ^ x_swizzle(c)).  The 64
-// banks of 4 bytes span 16 slots.  With XQ = 4 the slot of lane l (chunk
-// c0 + l, c0 a multiple of 16) is 4*(l & 3) + (q ^ (l >> 2)) mod 16; with
-// XQ = 2 it is 2*(l & 7) + (q ^ (l >> 3)): distinct for the 16 lanes either
-// way, with no padding.
+// LDS layout of staged activations: batch entry (or slot) b, chunk c, piece q
+// (16 bytes) sits at 16-byte slot v * XQ + (q ^ x_swizzle(v)) with the flat
+// chunk index v = b * nchunks + c; writers and readers both swizzle by v.  The
+// 64 banks of 4 bytes span 16 slots.  16 lanes reading chunks v0 .. v0 + 15
+// (any v0) cover every residue of v mod 16: with XQ = 4 lane slots are
+// 4*(v & 3) + (q ^ ((v >> 2) & 3)) mod 16, with XQ = 2 they are
+// 2*(v & 7) + (q ^ ((v >> 3) & 1)), distinct either way, with no padding.
 template <int FMT, int CB>
 __host__ __device__ constexpr int x_swizzle(int64_t c) {
     return ChunkShape<FMT, CB>::XQ == 4 ? (int)((c >> 2) & 3) : (ChunkShape<FMT, CB>::XQ == 2 ? (int)((c >> 3) & 1) : 0);
@@ -158,7 +159,8 @@ __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t 
                 if (t < pieces) {
                     const int64_t c = t / CS::XQ;
                     const int q = (int)(t % CS::XQ);
-                    dst[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v[u];
+                    const int64_t v_flat = (int64_t)b * (pieces / CS::XQ) + c;  // b * nchunks + c
+                    dst[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(v_flat))] = v[u];
                 }
             }
         }
@@ -220,7 +222,11 @@ struct RowCursor {
     const uint8_t* dummy;
 };
 
-template <int FMT, int CB, int B, int G, int S, int R, bool XL>
+// With SLOTS the S groups of a row set do not split one row: group s streams
+// all of its own row (the caller points each lane's `codes`/`scales` at its
+// group's matrix), against activation vector s of the staged LDS block (B must
+// be 1), and the S partial sums are combined with per-group multipliers.
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool SLOTS = false>
 struct RowEngine {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
@@ -245,8 +251,8 @@ struct RowEngine {
         rowbytes = code_bytes_per_row(FMT, k);
         sbytes = k / CS::BS;
         nchunks = rowbytes / CB;
-        step = (int64_t)S * G;
-        c0 = (int64_t)sp * G + lane;
+        step = SLOTS ? (int64_t)G : (int64_t)S * G;
+        c0 = SLOTS ? (int64_t)lane : (int64_t)sp * G + lane;
         niter = (nchunks + step - 1) / step;  // the same for every lane
     }
 
@@ -283,9 +289,10 @@ struct RowEngine {
         uint32_t xw[B][CS::NP];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const u32x4_t* xp = XL ? reinterpret_cast<const u32x4_t*>(xlds) + ((int64_t)b * nchunks + c) * CS::XQ
+            const int64_t vc = (SLOTS ? (int64_t)sp : (int64_t)b) * nchunks + c;  // chunk of the staged block
+            const u32x4_t* xp = XL ? reinterpret_cast<const u32x4_t*>(xlds) + vc * CS::XQ
                                    : reinterpret_cast<const u32x4_t*>(xs[b]) + c * CS::XQ;
-            const int swz = XL ? x_swizzle<FMT, CB>(c) : 0;
+            const int swz = XL ? x_swizzle<FMT, CB>(vc) : 0;
 #pragma unroll
             for (int q = 0; q < CS::XQ; ++q) {
                 const u32x4_t v = xp[q ^ swz];
@@ -326,9 +333,10 @@ struct RowEngine {
 
     // Sum over the G lanes and the S groups of the tile at row0 and store
     // ys[b][row] = gmul * sum (rows >= n are not written; ys[b] == nullptr
-    // skips entry b).
+    // skips entry b).  With SLOTS the groups' sums are weighted by smul[s] and
+    // groups s >= nslot are left out.
     __device__ __forceinline__ void finish(int64_t row0, float (&acc)[R][B], float* const (&ys)[B], float gmul,
-                                           float* red) const {
+                                           float* red, const float* smul = nullptr, int nslot = S) const {
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
@@ -342,7 +350,7 @@ struct RowEngine {
                     if (r < n) {
 #pragma unroll
                         for (int b = 0; b < B; ++b)
-                            if (ys[b]) ys[b][r] = acc[j][b] * gmul;
+                            if (ys[b]) ys[b][r] = SLOTS ? acc[j][b] * smul[0] : acc[j][b] * gmul;
                     }
                 }
             }
@@ -360,10 +368,18 @@ struct RowEngine {
                 if (r < n) {
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
-                        float v = red[(set * R + j) * B + b];
+                        if constexpr (SLOTS) {
+                            float v = red[(set * R + j) * B + b] * smul[0];
 #pragma unroll
-                        for (int s = 1; s < S; ++s) v += red[((s * T::ROWSETS + set) * R + j) * B + b];
-                        if (ys[b]) ys[b][r] = v * gmul;
+                            for (int s = 1; s < S; ++s)
+                                if (s < nslot) v += red[((s * T::ROWSETS + set) * R + j) * B + b] * smul[s];
+                            if (ys[b]) ys[b][r] = v;
+                        } else {
+                            float v = red[(set * R + j) * B + b];
+#pragma unroll
+                            for (int s = 1; s < S; ++s) v += red[((s * T::ROWSETS + set) * R + j) * B + b];
+                            if (ys[b]) ys[b][r] = v * gmul;
+                        }
                     }
                 }
             }
@@ -421,7 +437,8 @@ struct RowEngine {
     // of S*ROWSETS*R*B floats (unused when S == 1).
     template <int D>
     __device__ __forceinline__ void run(Cursor& u, PassRing<Pass, D + 1>& ring, const uint16_t* const (&xs)[B],
-                                        float* const (&ys)[B], float gmul, float* red, const uint8_t* xlds) const {
+                                        float* const (&ys)[B], float gmul, float* red, const uint8_t* xlds,
+                                        const float* smul = nullptr, int nslot = S) const {
         const int64_t total = u.count * niter;
         // compute cursor: tile tc, pass ic, chunk cc
         int64_t tc = 0, ic = 0;
@@ -435,7 +452,7 @@ struct RowEngine {
             compute(cur, cc, xs, xlds, acc);
             cc += (int)step;
             if (++ic == niter) {  // tile done: reduce and store
-                finish(u.first + tc * u.row_step, acc, ys, gmul, red);
+                finish(u.first + tc * u.row_step, acc, ys, gmul, red, smul, nslot);
 #pragma unroll
                 for (int j = 0; j < R; ++j)
 #pragma unroll

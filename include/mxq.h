@@ -156,10 +156,58 @@ mxq_status_t mxq_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, cons
 mxq_status_t mxq_dequant(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                          float *w, int64_t rows, int64_t k, void *stream);
 
+/*
+ * MoE routing (the step before the expert-indexed GEMV in a decode block):
+ * for each token t, the topk experts with the largest router logits are
+ * selected, larger first, equal logits lower index first (the selection
+ * compares the fp32 logits themselves, so it is exact); each gets its softmax
+ * probability over all experts, divided by the sum of the selected ones when
+ * `renorm` is nonzero.  Logits must not be NaN.
+ *   logits   fp32 [tokens][num_experts], num_experts 1 .. 1024
+ *   ids      int32 [tokens][topk] out;  weights fp32 [tokens][topk] out
+ *   tokens   1 .. MXQ_MAX_BATCH;  topk 1 .. min(MXQ_MAX_TOPK, num_experts)
+ */
+mxq_status_t mxq_moe_route(const float *logits, int32_t *expert_ids, float *weights, int64_t tokens,
+                           int64_t num_experts, int64_t topk, int renorm, void *stream);
+
+/*
+ * MoE decode block: the fused two-kernel path (gate/up, then down) that the
+ * "affine MoE" row of the ROCm status table of the manual describes for
+ * single-token decode:
+ *
+ *   h[t][s]    = W_gu[ids[t][s]] . x[t]                 (fp32, 2*dff outputs:
+ *                                                       gate rows 0..dff-1,
+ *                                                       up rows dff..2dff-1)
+ *   a[t][s][j] = bf16(silu(h[t][s][j]) * h[t][s][dff+j]) silu(g) = g/(1+e^-g),
+ *                                                       rounded to nearest even
+ *   y[t][i]    = sum_s weights[t][s] * sum_j W_dn[ids[t][s]][i][j] * a[t][s][j]
+ *
+ * Kernel 1 is mxq_moe_gemv on the gate/up bank (each routed expert read once,
+ * into the caller's workspace h); kernel 2 builds the activations in LDS and
+ * streams each output row of the token's routed down matrices, combining them
+ * in a fixed order.  A token with an expert id outside [0, num_experts) gets
+ * NaN outputs.
+ *   gu_codes/gu_scales  gate/up bank [num_experts][2*dff][hidden] (layout as mxq_moe_gemv)
+ *   dn_codes/dn_scales  down bank [num_experts][hidden][dff]
+ *   gu_gscale/dn_gscale NVFP4: fp32 [num_experts] each; MX: NULL
+ *   expert_ids int32 [tokens][topk]; weights fp32 [tokens][topk]
+ *   x        bf16 [tokens][hidden]
+ *   h        fp32 [tokens][topk][2*dff] workspace (caller-owned, 16-byte aligned)
+ *   y        fp32 [tokens][hidden]
+ *   hidden, dff multiples of the block size (32 MX, 16 NVFP4); tokens 1 .. MXQ_MAX_BATCH;
+ *   topk 1 .. MXQ_MAX_TOPK with topk rounded up to a power of two, times 2*dff
+ *   bytes, at most 64 KiB (else MXQ_E_UNSUPPORTED)
+ */
+mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales, const float *gu_gscale,
+                           const uint8_t *dn_codes, const uint8_t *dn_scales, const float *dn_gscale,
+                           const int32_t *expert_ids, const float *weights, const uint16_t *x, float *h, float *y,
+                           int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk,
+                           void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -62,6 +62,13 @@ def _load():
         lib.orc_gemv.argtypes = [I, P, P, P, P, I64, I64, I64, P, P]
         lib.orc_moe_gemv.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, I64, I64, P, P]
         lib.orc_gemm_rows.argtypes = [I, P, P, P, P, P, I64, I64, I64, P, P]
+        lib.orc_moe_route.argtypes = [P, I64, I64, I64, I, P, P]
+        lib.orc_silu.argtypes = [ctypes.c_double]
+        lib.orc_silu.restype = ctypes.c_double
+        lib.orc_round_bf16.argtypes = [ctypes.c_double]
+        lib.orc_round_bf16.restype = ctypes.c_double
+        D = ctypes.c_double
+        lib.orc_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, D, D, D, P, P, P]
         _lib = lib
     return _lib
 
@@ -153,6 +160,52 @@ def gemm_rows(fmt, codes, scales, g, X, rows, n, k):
     _load().orc_gemm_rows(fmt, _ptr(codes), _ptr(scales), _ptr(g), _ptr(X), _ptr(rows), rows.size, n, k,
                           _ptr(Y), _ptr(A))
     return Y, A
+
+
+def moe_route(logits, topk, renorm):
+    """(ids int32 [T][topk], weights fp64 [T][topk]) from fp32 router logits [T][E]:
+    the topk largest logits (ties: lower index first), softmax weights, optionally
+    renormalised over the selected experts."""
+    logits = _c(logits, np.float32)
+    tokens, experts = logits.shape
+    ids = np.empty((tokens, topk), dtype=np.int32)
+    w = np.empty((tokens, topk), dtype=np.float64)
+    _load().orc_moe_route(_ptr(logits), tokens, experts, topk, int(renorm), _ptr(ids), _ptr(w))
+    return ids, w
+
+
+def silu(g: float) -> float:
+    return _load().orc_silu(float(g))
+
+
+def round_bf16(v: float) -> float:
+    return _load().orc_round_bf16(float(v))
+
+
+def moe_block(fmt, gu_codes, gu_scales, gu_g, dn_codes, dn_scales, dn_g, ids, w, x, experts, hidden, dff,
+              rounding_tol=None):
+    """(y, abs_y), both fp64 [T][hidden]: the MoE decode block (gate/up, SwiGLU to bf16,
+    down, routing-weighted sum over the token's slots).
+
+    With ``rounding_tol = (h_rel, h_abs, p_rel)`` it returns (y, abs_y, amb_y):
+    amb_y bounds how far y may move when an implementation whose gate/up values
+    are within h_rel * sum|w x| + h_abs (plus their own fp32 rounding) and whose
+    fp32 SwiGLU is within p_rel relative rounds an activation to the other
+    bf16 neighbour."""
+    _check(fmt, hidden)
+    _check(fmt, dff)
+    gu_codes, gu_scales, gu_g = _c(gu_codes, np.uint8), _c(gu_scales, np.uint8), _c(gu_g, np.float32)
+    dn_codes, dn_scales, dn_g = _c(dn_codes, np.uint8), _c(dn_scales, np.uint8), _c(dn_g, np.float32)
+    ids, w, x = _c(ids, np.int32), _c(w, np.float32), _c(x, np.uint16)
+    tokens, topk = ids.shape
+    y = np.empty((tokens, hidden), dtype=np.float64)
+    a = np.empty((tokens, hidden), dtype=np.float64)
+    amb = None if rounding_tol is None else np.empty((tokens, hidden), dtype=np.float64)
+    h_rel, h_abs, p_rel = (0.0, 0.0, 0.0) if rounding_tol is None else map(float, rounding_tol)
+    _load().orc_moe_block(fmt, _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_g), _ptr(dn_codes), _ptr(dn_scales),
+                          _ptr(dn_g), _ptr(ids), _ptr(w), _ptr(x), experts, hidden, dff, tokens, topk,
+                          h_rel, h_abs, p_rel, _ptr(y), _ptr(a), _ptr(amb))
+    return (y, a) if amb is None else (y, a, amb)
 
 
 def within_tolerance(y_gpu, y_ref, abs_ref, rel=1e-5, atol=1e-6):

@@ -233,3 +233,157 @@ void orc_gemm_rows(int fmt, const uint8_t *codes, const uint8_t *scales, const f
         free(w);
     }
 }
+
+/* ---- MoE decode block: routing, gate/up + SwiGLU, down + weighted combine ----
+ *
+ * The "affine MoE" row of the ROCm status table in the "Build from source"
+ * manual describes single-token MoE decode as a fused two-kernel path (gate-up,
+ * then down); slide 13 of the talk lists the fused MoE port.  The pages give
+ * no formulas; the plain reading taken here:
+ *   routing:  p = softmax(logits) over the E experts; the k experts with the
+ *             largest logits are selected (larger first, equal logits: lower
+ *             index first); weight = p of the selected expert, divided by the
+ *             sum of the k selected p when `renorm` is set.
+ *   gate/up:  h[t][s] = fl32(W_gu[e] . x[t]), rows [0, dff) are the gate,
+ *             rows [dff, 2 dff) the up projection.
+ *   SwiGLU:   a[j] = bf16(fl32(fl32(silu(g_j)) * u_j)), silu(g) = g / (1 + exp(-g)):
+ *             evaluated in fp32, the precision of the gate/up values (silu
+ *             and the product each rounded to nearest), then rounded to the
+ *             nearest bf16, ties to even.  Taking the rounding decision on an
+ *             fp32 value matters at exact ties: for large g, silu(g) is g in
+ *             fp32, and g * u is often exactly halfway between bf16 numbers.
+ *   down:     y[t][i] = sum_s w[t][s] * sum_j W_dn[e_s][i][j] * a[t][s][j].
+ * abs_y = sum_s |w| sum_j |W a| is the acceptance scale.  An expert id
+ * outside [0, E) makes the token's y NaN.
+ *
+ * The bf16 rounding of a[j] is a decision taken on a value that a GPU computes
+ * with fp32 sums in its own order: where the exact product and a product
+ * within the stated error of it round to different bf16 numbers, both results
+ * are correct.  amb_y (optional) bounds what such decisions can move y:
+ *   delta_j = |silu'(g) u| eg + |silu(g)| eu + p_rel |p|,
+ *   eg = h_rel * sum|w x| + h_abs + 2^-24 |g|  (likewise eu; both 0 when
+ *        h_rel = h_abs = 0, which states that the gate/up sums are exact),
+ *   dev_j  = largest distance from a[j] of the bf16 rounding of any value in
+ *            [p - delta_j, p + delta_j] (rounding is monotone: the two ends),
+ *   amb_y[t][i] = sum_s |w| sum_j |W_dn[e_s][i][j]| dev_j.
+ * This is a bound on the acceptance test, not part of the block's result.
+ * parity of amb_y unpinned beyond its invariants (zero when delta is zero,
+ * covers every rounding inside the interval). */
+
+/* k largest of l[0..E) (ties: lower index first), in that order. */
+void orc_moe_route(const float *logits, int64_t tokens, int64_t experts, int64_t topk, int renorm,
+                   int32_t *ids, double *w)
+{
+    for (int64_t t = 0; t < tokens; ++t) {
+        const float *l = logits + t * experts;
+        double mx = -INFINITY;
+        for (int64_t e = 0; e < experts; ++e) mx = (double)l[e] > mx ? (double)l[e] : mx;
+        double den = 0.0;
+        for (int64_t e = 0; e < experts; ++e) den += exp((double)l[e] - mx);
+        double sel = 0.0;
+        for (int64_t s = 0; s < topk; ++s) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < experts; ++e) {
+                int taken = 0;
+                for (int64_t q = 0; q < s; ++q) taken |= ids[t * topk + q] == e;
+                if (taken) continue;
+                if (best < 0 || l[e] > l[best]) best = e;
+            }
+            ids[t * topk + s] = (int32_t)best;
+            w[t * topk + s] = exp((double)l[best] - mx) / den;
+            sel += w[t * topk + s];
+        }
+        if (renorm)
+            for (int64_t s = 0; s < topk; ++s) w[t * topk + s] /= sel;
+    }
+}
+
+double orc_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* Round to the nearest bf16 (ties to even), returned as a double. */
+double orc_round_bf16(double v)
+{
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    int e;
+    frexp(v, &e);                     /* |v| in [2^(e-1), 2^e) */
+    int emin = -125;                  /* bf16 normal range starts at 2^-126 = 2^(emin-1) */
+    int q = (e < emin ? emin : e) - 8; /* spacing of bf16 numbers near v: 2^q */
+    double r = ldexp(nearbyint(ldexp(v, -q)), q);  /* default rounding mode: to nearest even */
+    if (fabs(r) >= ldexp(1.0, 128) * (1.0 - ldexp(1.0, -9))) return v > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+void orc_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales, const float *gu_g,
+                   const uint8_t *dn_codes, const uint8_t *dn_scales, const float *dn_g,
+                   const int32_t *ids, const float *w, const uint16_t *x,
+                   int64_t experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk,
+                   double h_rel, double h_abs, double p_rel, double *y, double *abs_y, double *amb_y)
+{
+    const int64_t gcb = orc_code_bytes(fmt, hidden), gsb = hidden / orc_block(fmt);
+    const int64_t dcb = orc_code_bytes(fmt, dff), dsb = dff / orc_block(fmt);
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < tokens; ++t) {
+        double *a = (double *)malloc((size_t)(topk * dff) * sizeof(double));
+        double *dev = (double *)calloc((size_t)(topk * dff), sizeof(double));
+        int bad = 0;
+        for (int64_t s = 0; s < topk; ++s) {
+            const int64_t e = ids[t * topk + s];
+            if (e < 0 || e >= experts) { bad = 1; continue; }
+            const float gv = (fmt == ORC_NVFP4) ? gu_g[e] : 1.0f;
+            for (int64_t j = 0; j < dff; ++j) {
+                double hg, hu, ag, au;
+                orc_dot(fmt, gu_codes + (e * 2 * dff + j) * gcb, gu_scales + (e * 2 * dff + j) * gsb, gv,
+                        x + t * hidden, hidden, &hg, &ag);
+                orc_dot(fmt, gu_codes + (e * 2 * dff + dff + j) * gcb, gu_scales + (e * 2 * dff + dff + j) * gsb,
+                        gv, x + t * hidden, hidden, &hu, &au);
+                const double g32 = (double)(float)hg, u32 = (double)(float)hu;
+                const double s32 = (double)(float)orc_silu(g32);
+                const double p = (double)(float)(s32 * u32);  /* exact double product, one rounding */
+                a[s * dff + j] = orc_round_bf16(p);
+                if (amb_y) {
+                    const double sg = 1.0 / (1.0 + exp(-g32));            /* sigmoid */
+                    const double dsilu = sg * (1.0 + g32 * (1.0 - sg));  /* d silu / dg */
+                    /* h_rel = h_abs = 0 states that the gate/up values are exact in fp32 */
+                    const int inexact = h_rel > 0.0 || h_abs > 0.0;
+                    const double eg = inexact ? h_rel * ag + h_abs + ldexp(fabs(g32), -24) : 0.0;
+                    const double eu = inexact ? h_rel * au + h_abs + ldexp(fabs(u32), -24) : 0.0;
+                    const double d = fabs(dsilu * u32) * eg + fabs(orc_silu(g32)) * eu + p_rel * fabs(p);
+                    const double lo = fabs(orc_round_bf16(p - d) - a[s * dff + j]);
+                    const double hi = fabs(orc_round_bf16(p + d) - a[s * dff + j]);
+                    dev[s * dff + j] = lo > hi ? lo : hi;
+                }
+            }
+        }
+        for (int64_t i = 0; i < hidden; ++i) {
+            if (bad) {
+                y[t * hidden + i] = NAN;
+                abs_y[t * hidden + i] = NAN;
+                if (amb_y) amb_y[t * hidden + i] = NAN;
+                continue;
+            }
+            double acc = 0.0, aacc = 0.0, bacc = 0.0;
+            for (int64_t s = 0; s < topk; ++s) {
+                const int64_t e = ids[t * topk + s];
+                const float gv = (fmt == ORC_NVFP4) ? dn_g[e] : 1.0f;
+                const double ws = (double)w[t * topk + s];
+                double part = 0.0, apart = 0.0, bpart = 0.0;
+                for (int64_t j = 0; j < dff; ++j) {
+                    const double wv = (double)orc_weight(fmt, dn_codes + (e * hidden + i) * dcb,
+                                                         dn_scales + (e * hidden + i) * dsb, gv, j);
+                    part += wv * a[s * dff + j];
+                    apart += fabs(wv * a[s * dff + j]);
+                    bpart += fabs(wv) * dev[s * dff + j];
+                }
+                acc += ws * part;
+                aacc += fabs(ws) * apart;
+                bacc += fabs(ws) * bpart;
+            }
+            y[t * hidden + i] = acc;
+            abs_y[t * hidden + i] = aacc;
+            if (amb_y) amb_y[t * hidden + i] = bacc;
+        }
+        free(dev);
+        free(a);
+    }
+}

@@ -248,6 +248,200 @@ def check_gemm_rows_bruteforce(fmt):
             assert bf.close(A[i, c], (ex[1], ex[1]), k), (fmt, i, c)
 
 
+# ---- MoE decode block -------------------------------------------------------------
+
+def _route_reference(logits, topk, renorm):
+    """Pure-Python routing: order experts by (-logit, index), softmax with math.exp."""
+    ids, ws = [], []
+    for row in logits.astype(np.float64):
+        order = sorted(range(row.size), key=lambda e: (-row[e], e))[:topk]
+        mx = max(row)
+        den = math.fsum(math.exp(v - mx) for v in row)
+        w = [math.exp(row[e] - mx) / den for e in order]
+        if renorm:
+            tot = math.fsum(w)
+            w = [v / tot for v in w]
+        ids.append(order)
+        ws.append(w)
+    return np.array(ids, dtype=np.int32), np.array(ws, dtype=np.float64)
+
+
+def check_route():
+    rng = np.random.default_rng(31)
+    for topk in (1, 2, 4, 6):
+        for renorm in (False, True):
+            logits = rng.standard_normal(size=(4, 6)).astype(np.float32)
+            logits[1, 2] = logits[1, 4] = logits[1].max() + np.float32(1.0)  # tie at the top
+            logits[2, :] = np.float32(0.5)                                     # all equal
+            ids, w = oracle.moe_route(logits, topk, renorm)
+            ids_r, w_r = _route_reference(logits, topk, renorm)
+            assert (ids == ids_r).all(), (topk, renorm, ids, ids_r)
+            assert np.allclose(w, w_r, rtol=1e-14, atol=0.0), (topk, renorm)
+            if renorm:
+                assert np.allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def check_silu():
+    assert oracle.silu(0.0) == 0.0
+    for g in (0.25, 1.0, 3.5, 17.0):
+        # silu(-g) = -g * sigmoid(-g) = silu(g) - g
+        assert abs(oracle.silu(-g) - (oracle.silu(g) - g)) <= 1e-15 * max(1.0, g), g
+        assert abs(oracle.silu(g) - g / (1.0 + math.exp(-g))) <= 1e-16 * g
+    assert oracle.silu(60.0) == 60.0 * (1.0 / (1.0 + math.exp(-60.0)))
+    assert 0.0 > oracle.silu(-60.0) > -1e-20
+
+
+def check_round_bf16():
+    rng = np.random.default_rng(37)
+    f = np.concatenate([rng.standard_normal(4000).astype(np.float32) * np.float32(1e3),
+                        (np.arange(1, 512, dtype=np.float32) * np.float32(2.0 ** -8) + np.float32(1.0)),  # halfway points
+                        np.array([1e-39, -3e-40, 3.3e38, -3.39e38, 2.0 ** -133, 1.0 + 2.0 ** -8], dtype=np.float32)])
+    ref = torch.from_numpy(f).to(torch.bfloat16).float().numpy()
+    got = np.array([oracle.round_bf16(float(v)) for v in f])
+    assert (got == ref.astype(np.float64)).all(), np.argwhere(got != ref)[:5]
+
+
+def _moe_block_case(fmt, seed, E=5, H=64, dff=32, T=3, topk=2):
+    rng = np.random.default_rng(seed)
+    gu_codes, gu_scales, gu_g, _ = _rand_case(fmt, rng, E * 2 * dff, H)
+    dn_codes, dn_scales, dn_g, _ = _rand_case(fmt, rng, E * H, dff)
+    if fmt == NVFP4:
+        gu_g = (rng.random(E).astype(np.float32) + np.float32(0.25)).astype(np.float32)
+        dn_g = (rng.random(E).astype(np.float32) + np.float32(0.25)).astype(np.float32)
+    ids = np.stack([rng.choice(E, size=topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random(size=(T, topk)).astype(np.float32) + np.float32(0.1)
+    f = rng.standard_normal(size=(T, H), dtype=np.float32)
+    x = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    return dict(gu=(gu_codes.reshape(E, 2 * dff, -1), gu_scales.reshape(E, 2 * dff, -1), gu_g),
+                dn=(dn_codes.reshape(E, H, -1), dn_scales.reshape(E, H, -1), dn_g),
+                ids=ids, w=w, x=x, E=E, H=H, dff=dff, T=T, topk=topk)
+
+
+def _moe_block_composed(fmt, c):
+    """The block from already-pinned pieces: the MoE GEMV for gate/up and down, and
+    numpy / torch for the SwiGLU and its bf16 rounding."""
+    E, H, dff, T, topk = c["E"], c["H"], c["dff"], c["T"], c["topk"]
+    h, _ = oracle.moe_gemv(fmt, *c["gu"], c["ids"], c["x"], 0, E, 2 * dff, H)
+    h32 = h.astype(np.float32)
+    g, u = h32[..., :dff], h32[..., dff:]
+    with np.errstate(over="ignore", invalid="ignore"):
+        g64 = g.astype(np.float64)
+        silu32 = (g64 / (1.0 + np.exp(-g64))).astype(np.float32)   # silu rounded to fp32
+        act = torch.from_numpy(silu32 * u).to(torch.bfloat16)        # fp32 product, then RNE to bf16
+    a_bits = act.view(torch.int16).numpy().view(np.uint16).copy()
+    yd, ad = oracle.moe_gemv(fmt, *c["dn"], c["ids"], a_bits, 1, E, H, dff)
+    w = c["w"].astype(np.float64)[..., None]
+    return (w * yd).sum(axis=1), (np.abs(w) * ad).sum(axis=1)
+
+
+def check_moe_block(fmt, seed=41):
+    c = _moe_block_case(fmt, seed)
+    y, a = oracle.moe_block(fmt, *c["gu"], *c["dn"], c["ids"], c["w"], c["x"], c["E"], c["H"], c["dff"])
+    y_c, a_c = _moe_block_composed(fmt, c)
+    assert np.isfinite(y).all()
+    assert (np.abs(y - y_c) <= 1e-12 * a_c).all(), np.abs(y - y_c).max()
+    assert (np.abs(a - a_c) <= 1e-12 * a_c).all()
+    bad = c["ids"].copy()
+    bad[1, 0] = c["E"]
+    y2, _ = oracle.moe_block(fmt, *c["gu"], *c["dn"], bad, c["w"], c["x"], c["E"], c["H"], c["dff"])
+    assert np.isnan(y2[1]).all() and np.isfinite(y2[0]).all() and np.isfinite(y2[2]).all()
+
+
+def _one_block(fmt, gate_row0, up_row0, x_vals, H=32, dff=32):
+    """A one-expert MXFP4 block: gate row 0 and up row 0 (rows 0 and dff of the
+    gate/up bank) as given lists of (element, code, scale byte), x from exact
+    bf16 values, the down row 0 equal to 1.0 on element 0; every other weight 0."""
+    gc = np.zeros((1, 2 * dff, H // 2), dtype=np.uint8)
+    gs = np.full((1, 2 * dff, H // 32), 127, dtype=np.uint8)
+    for row, elems in ((0, gate_row0), (dff, up_row0)):
+        for k, code, scale in elems:
+            gc[0, row, k // 2] |= code << (4 * (k % 2))     # element 2i: low nibble
+            gs[0, row, k // 32] = scale
+    dc = np.zeros((1, H, dff // 2), dtype=np.uint8)
+    ds = np.full((1, H, dff // 32), 127, dtype=np.uint8)
+    dc[0, 0, 0] = 0x02                                        # W_dn[0][0] = 1.0
+    f = np.zeros((1, H), dtype=np.float32)
+    f[0, :len(x_vals)] = x_vals
+    x = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    ids = np.zeros((1, 1), dtype=np.int32)
+    w = np.ones((1, 1), dtype=np.float32)
+    y, _ = oracle.moe_block(fmt, gc, gs, None, dc, ds, None, ids, w, x, 1, H, dff)
+    return y[0]
+
+
+def check_swiglu_tie():
+    """Gate g = 32 (E2M1 4.0 at scale 2^3), x = (1, 2^-7, 2^-8): silu(32) is 32 in
+    fp32, so a = bf16(32 u) with u = 2^-5 (1 + 2^-7 + 2^-8) (three E2M1 1.0 at
+    scale 2^-5) is 1 + 2^-7 + 2^-8, exactly halfway between the bf16 numbers
+    1 + 2^-7 and 1 + 2^-6: ties to even give 1 + 2^-6.  With one more 2^-8 dropped
+    (u = 2^-5 (1 + 2^-8)) the tie is between 1 and 1 + 2^-7: even is 1.
+    y[0] = a (one expert, weight 1, W_dn row 0 = e_0); every other y is 0."""
+    gate = [(0, 0x6, 130)]
+    xv = [1.0, 2.0 ** -7, 2.0 ** -8]
+    y = _one_block(MXFP4, gate, [(0, 0x2, 122), (1, 0x2, 122), (2, 0x2, 122)], xv)
+    assert y[0] == 1.0 + 2.0 ** -6 and (y[1:] == 0).all(), y[:4]
+    y = _one_block(MXFP4, gate, [(0, 0x2, 122), (2, 0x2, 122)], xv)
+    assert y[0] == 1.0, y[0]
+    y = _one_block(MXFP4, gate, [(0, 0xA, 122), (1, 0xA, 122), (2, 0xA, 122)], xv)  # sign bit: u < 0
+    assert y[0] == -(1.0 + 2.0 ** -6), y[0]
+    y = _one_block(MXFP4, [(0, 0xE, 130)], [(0, 0x2, 122)], xv)                       # g = -32: silu ~ -4e-13
+    assert y[0] <= 0.0 and abs(y[0]) < 1e-12, y[0]
+
+
+def _block_fp32(c, rounding="rne"):
+    """The block as an fp32 implementation computes it (torch on the CPU, its own
+    summation order, silu as g / (1 + exp(-g)) in fp32), MXFP4 weights decoded by
+    the pinned dequantiser.  ``rounding``: "rne" (correct), "trunc" or "none"
+    (planted mistakes in the activation rounding)."""
+    E, H, dff = c["experts"], c["hidden"], c["dff"]
+    gc, gs, _ = c["gu"]
+    dc, ds, _ = c["dn"]
+    Wgu = torch.from_numpy(oracle.dequant(MXFP4, gc.reshape(E * 2 * dff, -1), gs.reshape(E * 2 * dff, -1), None,
+                                          E * 2 * dff, H)).reshape(E, 2 * dff, H)
+    Wdn = torch.from_numpy(oracle.dequant(MXFP4, dc.reshape(E * H, -1), ds.reshape(E * H, -1), None,
+                                          E * H, dff)).reshape(E, H, dff)
+    x = torch.from_numpy(c["x"].view(np.int16)).view(torch.bfloat16).float()
+    y = torch.zeros(c["tokens"], H)
+    for t in range(c["tokens"]):
+        for s in range(c["topk"]):
+            e = int(c["ids"][t, s])
+            h = Wgu[e] @ x[t]
+            g, u = h[:dff], h[dff:]
+            p = g / (1.0 + torch.exp(-g)) * u
+            if rounding == "rne":
+                a = p.to(torch.bfloat16).float()
+            elif rounding == "trunc":
+                a = (p.view(torch.int32) & ~0xFFFF).view(torch.float32)
+            else:
+                a = p
+            y[t] += float(c["w"][t, s]) * (Wdn[e] @ a)
+    return y.double().numpy()
+
+
+ROUNDING_TOL_EXACT = (0.0, 0.0, 2.0 ** -21)      # gate/up exact; fp32 SwiGLU within 8 ulp
+ROUNDING_TOL_CONTRACT = (1e-5, 1e-6, 2.0 ** -21)  # gate/up within the GEMV acceptance bound
+
+
+def check_block_rounding_bound():
+    """amb_y covers an fp32 implementation's choice of bf16 neighbour and no more
+    than that: the correct fp32 block passes |y - y_ref| <= 1e-5 abs + amb + 1e-6,
+    truncated or unrounded activations fail it; amb is 0 when nothing is uncertain."""
+    import synth
+    for exact, tol in ((True, ROUNDING_TOL_EXACT), (False, ROUNDING_TOL_CONTRACT)):
+        c = synth.moe_block(4, seed=17, experts=6, hidden=512, dff=256, topk=4, exact=exact)
+        args = (MXFP4, *c["gu"], *c["dn"], c["ids"], c["w"], c["x"], c["experts"], c["hidden"], c["dff"])
+        y, a, amb = oracle.moe_block(*args, rounding_tol=tol)
+        y0, a0, amb0 = oracle.moe_block(*args, rounding_tol=(0.0, 0.0, 0.0))
+        assert (y0 == y).all() and (a0 == a).all() and (amb0 == 0).all()
+        assert (amb >= 0).all() and np.isfinite(amb).all()
+        bound = 1e-5 * a + amb + 1e-6
+        assert (np.abs(_block_fp32(c) - y) <= bound).all(), exact
+        for bad in ("trunc", "none"):
+            assert (np.abs(_block_fp32(c, bad) - y) > bound).sum() > y.size // 10, (exact, bad)
+        if exact:
+            assert np.median(amb / a) < 1e-7
+
+
 def all_checks():
     """(name, callable) for every pin, used by the mutation test."""
     out = [("e2m1_table", check_e2m1_table), ("e8m0", check_e8m0), ("e4m3", check_e4m3),
@@ -259,5 +453,8 @@ def all_checks():
                 (f"one_hot_{f}", lambda f=f: check_one_hot(f)),
                 (f"scale_bump_{f}", lambda f=f: check_scale_bump(f)),
                 (f"moe_{f}", lambda f=f: check_moe_bruteforce(f, 1)),
-                (f"gemm_rows_{f}", lambda f=f: check_gemm_rows_bruteforce(f))]
+                (f"gemm_rows_{f}", lambda f=f: check_gemm_rows_bruteforce(f)),
+                (f"moe_block_{f}", lambda f=f: check_moe_block(f))]
+    out += [("route", check_route), ("silu", check_silu), ("round_bf16", check_round_bf16),
+            ("swiglu_tie", check_swiglu_tie), ("block_rounding_bound", check_block_rounding_bound)]
     return out

@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_status_string", "mxq_abi_version"])
+        ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
+         "mxq_status_string", "mxq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 1
+    assert lib.mxq_abi_version() == 2
 
 
 def test_status_strings():
@@ -59,7 +60,17 @@ def deq(fmt=1, codes=A, scales=A, g=None, w=A, rows=4, k=64):
     return mxq.lib().mxq_dequant(fmt, codes, scales, g, w, rows, k, None)
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq])
+def route(logits=A, ids=A, w=A, T=1, E=8, topk=2, renorm=0):
+    return mxq.lib().mxq_moe_route(logits, ids, w, T, E, topk, renorm, None)
+
+
+def block(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=None, ids=A, w=A, x=A, h=A, y=A,
+          E=4, hidden=64, dff=64, T=1, topk=2):
+    return mxq.lib().mxq_moe_block(fmt, codes, scales, g, dn_codes, dn_scales, dn_g, ids, w, x, h, y,
+                                   E, hidden, dff, T, topk, None)
+
+
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block])
 def test_format_errors(call):
     assert call(fmt=0) == FORMAT
     assert call(fmt=4) == FORMAT
@@ -68,7 +79,7 @@ def test_format_errors(call):
     assert call(fmt=2, g=A) == FORMAT
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq])
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block])
 def test_null_pointers(call):
     assert call(codes=None) == NULLPTR
     assert call(scales=None) == NULLPTR
@@ -79,6 +90,9 @@ def test_null_pointers_per_entry():
     assert moe(ids=None) == NULLPTR and moe(x=None) == NULLPTR and moe(y=None) == NULLPTR
     assert gemm(x=None) == NULLPTR and gemm(y=None) == NULLPTR
     assert deq(w=None) == NULLPTR
+    assert route(logits=None) == NULLPTR and route(ids=None) == NULLPTR and route(w=None) == NULLPTR
+    for arg in ("dn_codes", "dn_scales", "ids", "w", "x", "h", "y"):
+        assert block(**{arg: None}) == NULLPTR, arg
 
 
 def test_shape_errors():
@@ -92,6 +106,15 @@ def test_shape_errors():
     assert gemv(fmt=3, g=A, k=40) == SHAPE
     assert moe(fmt=1, k=16) == SHAPE and deq(fmt=2, k=80) == SHAPE
     assert gemm(fmt=3, g=A, k=48) == SHAPE
+    for bad in (0, -1):
+        assert route(T=bad) == SHAPE and route(E=bad) == SHAPE and route(topk=bad) == SHAPE
+        assert block(E=bad) == SHAPE and block(hidden=bad) == SHAPE and block(dff=bad) == SHAPE
+        assert block(T=bad) == SHAPE and block(topk=bad) == SHAPE
+    assert route(E=4, topk=5) == SHAPE                      # more picks than experts
+    assert block(hidden=48) == SHAPE and block(dff=80) == SHAPE
+    assert block(fmt=3, g=A, dn_g=A, dff=40) == SHAPE
+    # the two banks of one block share the format: its per-tensor scales go with it
+    assert block(fmt=3, g=A, dn_g=None) == FORMAT and block(fmt=1, dn_g=A) == FORMAT
 
 
 def test_alignment_errors():
@@ -100,6 +123,10 @@ def test_alignment_errors():
     assert moe(ids=A + 2) == ALIGN and moe(codes=A + 4) == ALIGN and moe(x=A + 8) == ALIGN
     assert gemm(x=A + 4) == ALIGN and gemm(y=A + 1) == ALIGN
     assert deq(w=A + 2) == ALIGN and deq(codes=A + 1) == ALIGN
+    assert route(logits=A + 2) == ALIGN and route(ids=A + 1) == ALIGN and route(w=A + 3) == ALIGN
+    for arg, off in (("codes", 8), ("dn_codes", 4), ("x", 8), ("h", 4), ("y", 2), ("ids", 2), ("w", 1)):
+        assert block(**{arg: A + off}) == ALIGN, arg
+    assert block(fmt=3, g=A, dn_g=A + 2) == ALIGN
 
 
 def test_unsupported_sizes():
@@ -107,6 +134,11 @@ def test_unsupported_sizes():
     assert gemv(n=1 << 31) == UNSUPPORTED
     assert moe(T=9) == UNSUPPORTED and moe(topk=17) == UNSUPPORTED
     assert gemm(m=1 << 31) == UNSUPPORTED
+    assert route(T=9) == UNSUPPORTED and route(E=1025, topk=2) == UNSUPPORTED and route(E=32, topk=17) == UNSUPPORTED
+    assert block(T=9) == UNSUPPORTED and block(E=32, topk=17) == UNSUPPORTED
+    # activations of the padded slot count staged in 64 KiB of LDS: 8 slots x 4096 x 2 bytes fit, 4128 do not
+    assert block(topk=8, dff=4128) == UNSUPPORTED and block(topk=5, dff=4128) == UNSUPPORTED
+    assert block(topk=4, dff=8224) == UNSUPPORTED and block(topk=2, dff=16416) == UNSUPPORTED
 
 
 def _no_gpu():
@@ -117,6 +149,8 @@ def _no_gpu():
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is present (it would launch on fake pointers)")
 def test_device_error_without_gpu():
     assert gemv() == DEVICE and moe() == DEVICE and gemm() == DEVICE and deq() == DEVICE
+    assert route() == DEVICE and block() == DEVICE
+    assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
 
 

@@ -35,6 +35,15 @@ MUTANTS = {
     "gemm_dropped_term": ("double t = (double)w[j] * orc_bf16(xr[j]);", "double t = (j + 1 < k) ? (double)w[j] * orc_bf16(xr[j]) : 0.0;"),
     "gemv_output_transposed": ("x + b * k, k, &y[b * n + r], &abs_y[b * n + r]", "x + b * k, k, &y[r * batch + b], &abs_y[r * batch + b]"),
     "bf16_shift": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
+    "route_tie_order": ("if (best < 0 || l[e] > l[best]) best = e;", "if (best < 0 || l[e] >= l[best]) best = e;"),
+    "route_no_renorm": ("w[t * topk + s] /= sel;", "w[t * topk + s] /= 1.0;"),
+    "route_softmax_shift": ("den += exp((double)l[e] - mx);", "den += exp((double)l[e]);"),
+    "silu_sign": ("return g / (1.0 + exp(-g));", "return g / (1.0 + exp(g));"),
+    "bf16_round_spacing": ("int q = (e < emin ? emin : e) - 8;", "int q = (e < emin ? emin : e) - 9;"),
+    "block_silu_on_up": ("(double)(float)orc_silu(g32);", "(double)(float)orc_silu(u32);"),
+    "block_weight_dropped": ("acc += ws * part;", "acc += part;"),
+    "block_no_bf16": ("a[s * dff + j] = orc_round_bf16(p);", "a[s * dff + j] = p;"),
+    "block_fp64_swiglu": ("const double p = (double)(float)(s32 * u32);", "const double p = orc_silu(g32) * u32;"),
 }
 
 
@@ -56,7 +65,8 @@ def test_pins_reject_mutant(tmp_path, monkeypatch, name):
     real = oracle._load()
     mutant = ctypes.CDLL(path)
     for attr in ("orc_e2m1", "orc_e8m0", "orc_e4m3", "orc_bf16", "orc_num_threads", "orc_set_num_threads",
-                 "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows"):
+                 "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows", "orc_moe_route", "orc_silu",
+                 "orc_round_bf16", "orc_moe_block"):
         fr, fm = getattr(real, attr), getattr(mutant, attr)
         fm.argtypes, fm.restype = fr.argtypes, fr.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
