@@ -79,7 +79,8 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 namespace mxq {
 
 // Dense GEMV kernel settings: chosen from the shape by the launcher unless
-// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu[,grid]" overrides them (used only to
+// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu[,grid]" or
+// MXQ_GEMV_MFMA="path[,r,ks,waves,wgs_per_cu]" overrides them (used only to
 // compare variants when tuning).
 GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
     (void)fmt, (void)n, (void)k, (void)batch;
@@ -92,6 +93,16 @@ GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
             c.rows_r = r;
             c.rows_occ = occ;
             c.rows_grid = grid;
+        }
+    }
+    if (const char* env = std::getenv("MXQ_GEMV_MFMA")) {
+        int path = 0, r = 0, ks = 0, nw = 0, occ = 0;
+        if (std::sscanf(env, "%d,%d,%d,%d,%d", &path, &r, &ks, &nw, &occ) >= 1) {
+            c.path = path;
+            c.mfma_r = r;
+            c.mfma_ks = ks;
+            c.mfma_nw = nw;
+            c.mfma_occ = occ;
         }
     }
     return c;

@@ -36,13 +36,12 @@
 
 #include "kernels.hpp"
 #include "mxq_device.hpp"
+#include "block_operand.hpp"
 #include "rows_core.hpp"
 
 namespace mxq {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4g_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 512;
@@ -55,75 +54,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
-}
-
-// Two E2M1 codes (byte SEL of w) times an arbitrary fp32 scale s, as a bf16 pair.
-template <int SEL>
-__device__ __forceinline__ uint32_t scaled_fp4x2_to_bf16x2(uint32_t w, float s) {
-    const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    const bf16x2_t b = {(__bf16)(f[0] * s), (__bf16)(f[1] * s)};
-    return __builtin_bit_cast(uint32_t, b);
-}
-
-// One lane's W codes for one slice: the 32 consecutive k of one row starting
-// at a multiple of 32, and their scale byte(s).
-template <int FMT>
-struct WFrag {
-    static constexpr int DW = (FMT == kMXFP8) ? 8 : 4;
-    uint32_t w[DW];
-    uint32_t s;  // one E8M0 byte, or two E4M3 bytes (NVFP4) in bits 7:0 and 15:8
-};
-
-// Elements past k read as zero codes (with a unit scale).
-template <int FMT>
-__device__ __forceinline__ void load_wfrag(const uint8_t* crow, const uint8_t* srow, int64_t kb, int64_t k,
-                                           WFrag<FMT>& f) {
-    if (kb >= k) {
-#pragma unroll
-        for (int i = 0; i < WFrag<FMT>::DW; ++i) f.w[i] = 0u;
-        f.s = FMT == kNVFP4 ? 0x3838u : 127u;
-        return;
-    }
-    if constexpr (FMT == kMXFP8) {
-        const u32x4g_t* q = reinterpret_cast<const u32x4g_t*>(crow + kb);
-        const u32x4g_t v0 = q[0], v1 = q[1];
-        f.w[0] = v0[0]; f.w[1] = v0[1]; f.w[2] = v0[2]; f.w[3] = v0[3];
-        f.w[4] = v1[0]; f.w[5] = v1[1]; f.w[6] = v1[2]; f.w[7] = v1[3];
-        f.s = srow[kb / 32];
-    } else {
-        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kb / 2);
-        f.w[0] = v[0]; f.w[1] = v[1]; f.w[2] = v[2]; f.w[3] = v[3];
-        if constexpr (FMT == kMXFP4) f.s = srow[kb / 32];
-        else f.s = (uint32_t)srow[kb / 16] | ((uint32_t)srow[kb / 16 + 1] << 8);
-    }
-}
-
-// The B operand of k step S: the fragment's codes S*8 .. S*8+7 as bf16.
-template <int FMT, int S>
-__device__ __forceinline__ bf16x8_t decode_step(const WFrag<FMT>& f) {
-    uint32_t d[4];
-    if constexpr (FMT == kMXFP4) {
-        const float se = e8m0_exponent(f.s);
-        d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.w[S], se, 0));
-        d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.w[S], se, 1));
-        d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.w[S], se, 2));
-        d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(f.w[S], se, 3));
-    } else if constexpr (FMT == kMXFP8) {
-        const float se = e8m0_exponent(f.s);
-        d[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.w[2 * S], se, false));
-        d[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.w[2 * S], se, true));
-        d[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.w[2 * S + 1], se, false));
-        d[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f.w[2 * S + 1], se, true));
-    } else {
-        // The conversion uses only the exponent of its scale operand, so the
-        // E4M3 block scale (16 elements: k steps 0-1, then 2-3) is applied in fp32.
-        const float s = e4m3_to_f32(S < 2 ? (f.s & 0xFFu) : ((f.s >> 8) & 0xFFu));
-        d[0] = scaled_fp4x2_to_bf16x2<0>(f.w[S], s);
-        d[1] = scaled_fp4x2_to_bf16x2<1>(f.w[S], s);
-        d[2] = scaled_fp4x2_to_bf16x2<2>(f.w[S], s);
-        d[3] = scaled_fp4x2_to_bf16x2<3>(f.w[S], s);
-    }
-    return __builtin_bit_cast(bf16x8_t, u32x4g_t{d[0], d[1], d[2], d[3]});
 }
 
 // Tile coordinates of workgroup b (XCD-aware grouped order): consecutive

@@ -5,6 +5,7 @@
 
 #include <atomic>
 
+#include "gemv_mfma.hpp"
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
@@ -137,6 +138,11 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
 
 template <int FMT, int CB>
 static bool launch_gemv_cb(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
+    // The FMA path spends one dot2 per two weights per batch entry; from batch
+    // 5 (the 8-vector instance) the matrix unit is faster at every dense
+    // shape measured on MI355X, below it the FMA path is.
+    const bool mfma = cfg.path == 1 || (cfg.path == 0 && a.batch >= 5);
+    if (mfma && a.k % 32 == 0) return launch_gemv_mfma<FMT>(a, cfg, st);
     if (a.batch <= 1) return launch_rows_b<FMT, CB, 1>(a, cfg, st);
     if (a.batch <= 2) return launch_rows_b<FMT, CB, 2>(a, cfg, st);
     if (a.batch <= 4) return launch_rows_b<FMT, CB, 4>(a, cfg, st);

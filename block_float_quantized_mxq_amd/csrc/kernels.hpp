@@ -26,6 +26,11 @@ struct GemvArgs {
 struct GemvConfig {
     int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
     int rows_grid = 0;  // 0: min(tiles, resident); 1: equal tiles per workgroup; 2: one workgroup per tile
+    // Path: 0 = by batch (matrix unit from batch 5), 1 = matrix unit, 2 = FMA rows.
+    int path = 0;
+    // Matrix-unit settings: rows per wave (x16), k split, waves per workgroup,
+    // workgroups per CU; mfma_ks == 0 = chosen from the shape.
+    int mfma_r = 0, mfma_ks = 0, mfma_nw = 0, mfma_occ = 0;
 };
 
 #define MXQ_ROWS_SHAPES(X) \

@@ -179,16 +179,20 @@ static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
 // MI355X measurements: rows of >= 64 chunks take 16 lanes and 2 rows per
-// lane; shorter rows take 8 lanes at one token and 4 lanes for more tokens
-// (more rows per workgroup for the same activations).  MXQ_MOE_ROWS="g,s,r"
-// overrides the choice (used only to compare variants when tuning).
+// lane up to two tokens and 8 lanes with one row per lane beyond; shorter
+// rows take 8 lanes up to two tokens and 4 lanes beyond (more rows per
+// workgroup for the same activations).  MXQ_MOE_ROWS="g,s,r" overrides the
+// choice (used only to compare variants when tuning).
 template <int FMT, int CB>
 static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
     int g = 16, sp = 1, r = 2;
     if (nchunks < 64) {
         r = 1;
-        g = (a.tokens == 1 && nchunks >= 8) ? 8 : 4;
+        g = (a.tokens <= 2 && nchunks >= 8) ? 8 : 4;
+    } else if (a.tokens >= 3) {
+        g = 8;
+        r = 1;
     }
     if (const char* env = std::getenv("MXQ_MOE_ROWS")) std::sscanf(env, "%d,%d,%d", &g, &sp, &r);
 #define MXQ_MOE_CASE(G_, S_, R_)                        \

@@ -195,3 +195,32 @@ def test_rejects_bad_arguments_on_gpu():
     assert e.value.status == 5
     with pytest.raises(ValueError):
         mxq.gemv(3, codes, torch.zeros(8, 2, dtype=torch.uint8, device="cuda:0"), x[:1])  # NVFP4 without g
+
+
+MFMA_SETTINGS = ["1,1,1,4,0", "1,2,1,4,0", "1,4,1,4,0", "1,1,2,4,0", "1,1,4,4,0", "1,2,4,4,0", "1,4,4,4,0", "1,2,8,8,0"]
+
+
+@pytest.mark.parametrize("setting", MFMA_SETTINGS)
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("n,k", [(1000, 5120), (77, 25600), (129, 768), (300, 96), (64, 4096)])
+def test_matrix_unit_settings_all_outputs(setting, fmt, n, k, monkeypatch):
+    """Every compiled (rows per wave, k split, waves) setting of the matrix-unit
+    GEMV, forced for batches 1, 3 and 8, every output checked (ragged row
+    blocks, k ranges that end inside a pass, empty k ranges)."""
+    monkeypatch.setenv("MXQ_GEMV_MFMA", setting)
+    sc, ss, sx, _, _ = synth.streams(7 * n + k + fmt)
+    codes, scales, g = synth.weights(fmt, sc, ss, n, k)
+    for batch in (1, 3, 8):
+        x = synth.bf16_normal(sx, (batch, k))
+        check_all(dict(fmt=fmt, codes=codes, scales=scales, g=g, x=x, n=n, k=k),
+                  f"matrix unit {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}")
+
+
+def test_matrix_unit_and_fma_paths_agree_at_batch_one(monkeypatch):
+    """The two GEMV paths on the same full-size gate/up input: each within the
+    acceptance bound of the oracle on sampled rows."""
+    case = synth.dense_layer("gate_up", 1, seed=3)
+    rows = sample_rows(case["n"], 256, seed=3)
+    for path in ("1", "2"):
+        monkeypatch.setenv("MXQ_GEMV_MFMA", path)
+        check_rows(case, rows, f"gate/up B=1 path {path}")
