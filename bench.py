@@ -15,7 +15,8 @@ value = weight bytes read per step / step time (GB/s).  The same JSON line
 carries: the roofline of the dominant kernel (the gate/up GEMV: a graph of
 back-to-back launches over the 64 distinct copies, timed with HIP events on
 the launch stream), the batch-4 step, the MoE GEMV (128-expert bank, top-8,
-1/2/4 tokens), the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
+1/2/4 tokens), the fused MoE decode block (routing, gate/up, SwiGLU, down and
+the weighted combine, same bank), the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
 fraction, a plain copy kernel for reference, and the CPU oracle timed on a
 bounded sample (cpu_baseline).
 
@@ -53,7 +54,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=LAYERS)
-    p.add_argument("--only", default="", help="comma list of parts: dense,moe,formats,gemm,copy,cpu")
+    p.add_argument("--only", default="", help="comma list of parts: dense,moe,moe_block,formats,gemm,copy,cpu")
     p.add_argument("--profile-kernel", default="", help="run one kernel eagerly for rocprofv3")
     return p.parse_args()
 
@@ -95,7 +96,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    all_parts = {"dense", "moe", "formats", "gemm", "copy", "cpu"}
+    all_parts = {"dense", "moe", "moe_block", "formats", "gemm", "copy", "cpu"}
     parts = set(args.only.split(",")) if args.only else all_parts
 
     def u8(a):
@@ -247,6 +248,45 @@ def main():
                 gbs=(moe[f"gate_up_T{T}"]["active_mb"] + moe[f"down_T{T}"]["active_mb"]) * 1e6 / t_layer / 1e9,
                 equiv_tok_s=T / (MOE_LAYERS * t_layer))
         extras["moe"] = {k: {kk: round(v, 3) for kk, v in d.items()} for k, d in moe.items()}
+
+    # ---------------- MoE decode block: routing -> gate/up -> SwiGLU -> down -> combine ----------------
+    if "moe_block" in parts:
+        mb = {}
+        copies = 4
+        gu_case = synth.moe_layer("gate_up", 1, seed=0)
+        dn_case = synth.moe_layer("down", 1, seed=0)
+        gu = [(u8(gu_case["codes"]), u8(gu_case["scales"])) for _ in range(copies)]
+        dn = [(u8(dn_case["codes"]), u8(dn_case["scales"])) for _ in range(copies)]
+        per_expert = mxq.weight_bytes(mxq.MXFP4, 1536, 2048) + mxq.weight_bytes(mxq.MXFP4, 2048, 768)
+        for T in (1, 2, 4):
+            _, _, sx, si, _ = synth.streams(200 + T)
+            nsets = 32
+            logits = [torch.from_numpy(synth.router_logits(si, T, 128)).to(dev) for _ in range(nsets)]
+            x = bf(synth.bf16_normal(sx, (T, 2048)))
+            ids = torch.empty((T, 8), dtype=torch.int32, device=dev)
+            wts = torch.empty((T, 8), dtype=torch.float32, device=dev)
+            h = torch.empty((T, 8, 1536), dtype=torch.float32, device=dev)
+            y = torch.empty((T, 2048), dtype=torch.float32, device=dev)
+            active = []
+            for lg in logits:  # union of routed experts per set (for the byte count only)
+                i, _ = mxq.moe_route(lg, 8, True)
+                active.append(len(np.unique(i.cpu().numpy())) * per_expert)
+            active = float(np.mean(active))
+
+            def fn():
+                for i in range(nsets):
+                    mxq.moe_route(logits[i], 8, True, ids=ids, weights=wts)
+                    mxq.moe_block(1, *gu[i % copies], *dn[i % copies], ids, wts, x, h=h, out=y)
+
+            us = timed_graph(fn, 8) * 1e3 / nsets
+            mb[f"T{T}"] = dict(us=round(us, 3), active_mb=round(active / 1e6, 3), gbs=round(active / (us * 1e-6) / 1e9, 1),
+                               pct_peak=round(100 * active / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                               equiv_tok_s=round(T / (MOE_LAYERS * us * 1e-6), 1))
+            log(f"moe block T={T}: {us:.2f} us (route + gate/up + SwiGLU/down/combine), {active / 1e6:.1f} MB active, "
+                f"{mb[f'T{T}']['gbs']:.0f} GB/s")
+        del gu, dn
+        torch.cuda.empty_cache()
+        extras["moe_block"] = mb
 
     # ---------------- format sweep at the down shape ----------------
     if "formats" in parts:

@@ -31,17 +31,30 @@ namespace mxq {
 
 // ---- routing ---------------------------------------------------------------------
 
-// Largest (value, index) pair of the wave, equal values: lower index.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(v, off, 64);
-        const int oi = __shfl_xor(i, off, 64);
-        if (ov > v || (ov == v && oi < i)) {
-            v = ov;
-            i = oi;
-        }
+__device__ __forceinline__ void take_better(float& v, int& i, float ov, int oi) {
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
     }
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Largest (value, index) pair of the wave, equal values: lower index; every
+// lane ends with it.  Inside each row of 16 lanes the partners come from DPP
+// (swap neighbours, swap pairs, mirror halves, mirror the row: each step
+// pairs every lane with one that holds the other half of its group), across
+// rows from two shuffles.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    take_better(v, i, dpp_f32<kDppQuadXor1>(v), dpp_i32<kDppQuadXor1>(i));
+    take_better(v, i, dpp_f32<kDppQuadXor2>(v), dpp_i32<kDppQuadXor2>(i));
+    take_better(v, i, dpp_f32<kDppRowHalfMirror>(v), dpp_i32<kDppRowHalfMirror>(i));
+    take_better(v, i, dpp_f32<kDppRowMirror>(v), dpp_i32<kDppRowMirror>(i));
+    take_better(v, i, __shfl_xor(v, 16, 64), __shfl_xor(i, 16, 64));
+    take_better(v, i, __shfl_xor(v, 32, 64), __shfl_xor(i, 32, 64));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -50,19 +63,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// One wave per token; lane l owns experts l, l + 64, ... (at most kRouteMaxPerLane).
+// One wave per token; lane l owns experts l, l + 64, ... (PL per lane, the
+// smallest power of two that covers the experts: a single wave runs this
+// serially, so its loops are sized to the expert count).
 constexpr int kRouteMaxPerLane = 16;  // experts <= 1024
 
+template <int PL>
 __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int64_t experts, int topk,
                                                        int renorm, int32_t* __restrict__ ids,
                                                        float* __restrict__ weights) {
     const int64_t t = blockIdx.x;
     const int lane = threadIdx.x;
     const float* l = logits + t * experts;
-    float v[kRouteMaxPerLane];
+    float v[PL];
     float mx = -__builtin_huge_valf();
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
         const int64_t e = (int64_t)i * 64 + lane;
         v[i] = e < experts ? l[e] : -__builtin_huge_valf();
         mx = v[i] > mx ? v[i] : mx;
@@ -71,7 +87,7 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
     wave_argmax(mx, dummy);
     float den = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i)
+    for (int i = 0; i < PL; ++i)
         if ((int64_t)i * 64 + lane < experts) den += expf(v[i] - mx);
     den = wave_sum(den);
     uint32_t taken = 0u;  // bit i: expert i*64 + lane already selected
@@ -80,7 +96,7 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
         float bv = -__builtin_huge_valf();
         int bi = 0x7FFFFFFF;
 #pragma unroll
-        for (int i = 0; i < kRouteMaxPerLane; ++i) {
+        for (int i = 0; i < PL; ++i) {
             const int64_t e = (int64_t)i * 64 + lane;
             if (e < experts && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7FFFFFFF)) {
                 bv = v[i];
@@ -99,8 +115,15 @@ __global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__
 
 bool launch_moe_route(const RouteArgs& a, hipStream_t st) {
     if (a.experts > 64 * kRouteMaxPerLane) return false;
-    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)a.tokens), dim3(64), 0, st, a.logits, a.experts, (int)a.topk,
-                       a.renorm, a.ids, a.weights);
+    const int pl = a.experts <= 64 ? 1 : a.experts <= 128 ? 2 : a.experts <= 256 ? 4 : a.experts <= 512 ? 8 : 16;
+    const dim3 grid((unsigned)a.tokens), block(64);
+    switch (pl) {
+        case 1: hipLaunchKernelGGL(moe_route_kernel<1>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
+        case 2: hipLaunchKernelGGL(moe_route_kernel<2>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
+        case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
+        case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
+        default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
+    }
     return true;
 }
 
@@ -161,18 +184,35 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t* __res
     eng.template prime<1>(cur, ring);  // weights first: in flight while the activations are built
 
     // activations of the token's slots, slot s at elements s*dff .. of the staged block
+    // (the h loads of U pieces per thread are issued together: one cache
+    // round trip per U pieces, not per piece)
+    constexpr int U = 3;
     const int64_t pieces = (int64_t)topk * dff / 8;
-    for (int64_t p = threadIdx.x; p < pieces; p += kThreads) {
-        const int64_t s = p * 8 / dff, j = p * 8 % dff;
-        const float* hg = h + (t * topk + s) * 2 * dff + j;
-        const float* hu = hg + dff;
-        const float4 g0 = *reinterpret_cast<const float4*>(hg), g1 = *reinterpret_cast<const float4*>(hg + 4);
-        const float4 u0 = *reinterpret_cast<const float4*>(hu), u1 = *reinterpret_cast<const float4*>(hu + 4);
-        const u32x4_t v = {swiglu_bf16x2(g0.x, u0.x, g0.y, u0.y), swiglu_bf16x2(g0.z, u0.z, g0.w, u0.w),
-                           swiglu_bf16x2(g1.x, u1.x, g1.y, u1.y), swiglu_bf16x2(g1.z, u1.z, g1.w, u1.w)};
-        const int64_t c = p / CS::XQ;
-        const int q = (int)(p % CS::XQ);
-        reinterpret_cast<u32x4_t*>(xlds)[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v;
+    for (int64_t p0 = threadIdx.x; p0 < pieces; p0 += U * kThreads) {
+        float4 g[U][2], u[U][2];
+#pragma unroll
+        for (int w = 0; w < U; ++w) {
+            const int64_t p = p0 + (int64_t)w * kThreads;
+            const int64_t pp = p < pieces ? p : p0;
+            const int64_t s = pp * 8 / dff, j = pp * 8 % dff;
+            const float* hg = h + (t * topk + s) * 2 * dff + j;
+            g[w][0] = *reinterpret_cast<const float4*>(hg);
+            g[w][1] = *reinterpret_cast<const float4*>(hg + 4);
+            u[w][0] = *reinterpret_cast<const float4*>(hg + dff);
+            u[w][1] = *reinterpret_cast<const float4*>(hg + dff + 4);
+        }
+#pragma unroll
+        for (int w = 0; w < U; ++w) {
+            const int64_t p = p0 + (int64_t)w * kThreads;
+            if (p < pieces) {
+                const float4 g0 = g[w][0], g1 = g[w][1], u0 = u[w][0], u1 = u[w][1];
+                const u32x4_t v = {swiglu_bf16x2(g0.x, u0.x, g0.y, u0.y), swiglu_bf16x2(g0.z, u0.z, g0.w, u0.w),
+                                   swiglu_bf16x2(g1.x, u1.x, g1.y, u1.y), swiglu_bf16x2(g1.z, u1.z, g1.w, u1.w)};
+                const int64_t c = p / CS::XQ;
+                const int q = (int)(p % CS::XQ);
+                reinterpret_cast<u32x4_t*>(xlds)[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v;
+            }
+        }
     }
     lds_barrier();
     eng.template run<1>(cur, ring, xs, ys, 1.0f, red, xlds, smul, topk);

@@ -47,7 +47,8 @@ def route_case(seed, tokens, experts):
 
 
 @pytest.mark.parametrize("tokens,experts,topk", [(1, 128, 8), (4, 128, 8), (8, 128, 8), (3, 64, 6), (2, 6, 6),
-                                                 (5, 1000, 16), (2, 1024, 1), (8, 200, 3), (3, 65, 5)])
+                                                 (5, 1000, 16), (2, 1024, 1), (8, 200, 3), (3, 65, 5), (2, 300, 8),
+                                                 (1, 512, 4)])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_route(tokens, experts, topk, renorm):
     logits = route_case(tokens * 1000 + experts, tokens, experts)
