@@ -18,10 +18,10 @@
 //    routing weights in a fixed order -- no atomics, bit-reproducible.
 //  * a token with an expert id outside [0, E) gets NaN outputs.
 //
-// Routing: one wave per token.  Selection compares the fp32 logits themselves
-// (larger first, equal logits: lower index first), so it does not depend on
-// how the softmax is rounded; the weights are the softmax probabilities of the
-// selected experts, optionally renormalised over them.
+// Routing: one workgroup per token.  Selection compares the fp32 logits
+// themselves (larger first, equal logits: lower index first), so it does not
+// depend on how the softmax is rounded; the weights are the softmax
+// probabilities of the selected experts, optionally renormalised over them.
 #include <cstdlib>
 
 #include "kernels.hpp"
@@ -57,73 +57,84 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     take_better(v, i, __shfl_xor(v, 32, 64), __shfl_xor(i, 32, 64));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// One workgroup per token.  The logits go to LDS; each expert's rank is the
+// number of logits that beat it (larger, or equal with a lower index), so the
+// selected experts are those of rank < topk and the rank is their output
+// slot -- the same order as picking the largest remaining logit topk times,
+// without topk serial rounds.  The softmax maximum and denominator are
+// workgroup reductions; the renormalising sum adds the selected
+// probabilities in slot order.
+constexpr int kRouteThreads = 256;
+constexpr int kRouteMaxExperts = 1024;
+
+__device__ __forceinline__ float wave_max(float v) {
+    int dummy = 0;
+    wave_argmax(v, dummy);
     return v;
 }
 
-// One wave per token; lane l owns experts l, l + 64, ... (PL per lane, the
-// smallest power of two that covers the experts: a single wave runs this
-// serially, so its loops are sized to the expert count).
-constexpr int kRouteMaxPerLane = 16;  // experts <= 1024
-
-template <int PL>
-__global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int64_t experts, int topk,
-                                                       int renorm, int32_t* __restrict__ ids,
-                                                       float* __restrict__ weights) {
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* __restrict__ logits, int64_t experts,
+                                                                  int topk, int renorm, int32_t* __restrict__ ids,
+                                                                  float* __restrict__ weights) {
+    __shared__ __attribute__((aligned(16))) float lv[kRouteMaxExperts];
+    __shared__ float part[kRouteThreads / 64];
+    __shared__ float psel[16];
     const int64_t t = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int E = (int)experts;
     const float* l = logits + t * experts;
-    float v[PL];
+
     float mx = -__builtin_huge_valf();
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        const int64_t e = (int64_t)i * 64 + lane;
-        v[i] = e < experts ? l[e] : -__builtin_huge_valf();
-        mx = v[i] > mx ? v[i] : mx;
+    for (int e = tid; e < E; e += kRouteThreads) {
+        const float v = l[e];
+        lv[e] = v;
+        mx = v > mx ? v : mx;
     }
-    int dummy = 0;
-    wave_argmax(mx, dummy);
+    for (int e = E + tid; e < ((E + 3) & ~3); e += kRouteThreads) lv[e] = -__builtin_huge_valf();  // pad to 4
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) part[wave] = mx;
+    __syncthreads();
+    mx = part[0];
+#pragma unroll
+    for (int w = 1; w < kRouteThreads / 64; ++w) mx = part[w] > mx ? part[w] : mx;
+    __syncthreads();  // part is reused below
+
     float den = 0.0f;
+    for (int e = tid; e < E; e += kRouteThreads) den += expf(lv[e] - mx);
+    den = group_sum<64>(den);
+    if ((tid & 63) == 0) part[wave] = den;
+    __syncthreads();
+    den = part[0];
 #pragma unroll
-    for (int i = 0; i < PL; ++i)
-        if ((int64_t)i * 64 + lane < experts) den += expf(v[i] - mx);
-    den = wave_sum(den);
-    uint32_t taken = 0u;  // bit i: expert i*64 + lane already selected
-    float sel = 0.0f, wsel = 0.0f;
-    for (int s = 0; s < topk; ++s) {
-        float bv = -__builtin_huge_valf();
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int64_t e = (int64_t)i * 64 + lane;
-            if (e < experts && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7FFFFFFF)) {
-                bv = v[i];
-                bi = (int)e;
-            }
+    for (int w = 1; w < kRouteThreads / 64; ++w) den += part[w];
+
+    for (int e = tid; e < E; e += kRouteThreads) {
+        const float v = lv[e];
+        int rank = 0;
+        for (int j = 0; j < E; j += 4) {
+            const float4 o = *reinterpret_cast<const float4*>(lv + j);
+            rank += (o.x > v || (o.x == v && j < e)) ? 1 : 0;
+            rank += (o.y > v || (o.y == v && j + 1 < e)) ? 1 : 0;
+            rank += (o.z > v || (o.z == v && j + 2 < e)) ? 1 : 0;
+            rank += (o.w > v || (o.w == v && j + 3 < e)) ? 1 : 0;
         }
-        wave_argmax(bv, bi);
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        const float p = expf(bv - mx) / den;
-        sel += p;
-        if (lane == s) wsel = p;
-        if (lane == 0) ids[t * topk + s] = bi;
+        if (rank < topk) {
+            ids[t * topk + rank] = e;
+            psel[rank] = expf(v - mx) / den;
+        }
     }
-    if (lane < topk) weights[t * topk + lane] = renorm ? wsel / sel : wsel;
+    __syncthreads();
+    if (tid < topk) {
+        float sel = 0.0f;
+        for (int s = 0; s < topk; ++s) sel += psel[s];
+        weights[t * topk + tid] = renorm ? psel[tid] / sel : psel[tid];
+    }
 }
 
 bool launch_moe_route(const RouteArgs& a, hipStream_t st) {
-    if (a.experts > 64 * kRouteMaxPerLane) return false;
-    const int pl = a.experts <= 64 ? 1 : a.experts <= 128 ? 2 : a.experts <= 256 ? 4 : a.experts <= 512 ? 8 : 16;
-    const dim3 grid((unsigned)a.tokens), block(64);
-    switch (pl) {
-        case 1: hipLaunchKernelGGL(moe_route_kernel<1>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
-        case 2: hipLaunchKernelGGL(moe_route_kernel<2>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
-        case 4: hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
-        case 8: hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
-        default: hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, st, a.logits, a.experts, (int)a.topk, a.renorm, a.ids, a.weights); break;
-    }
+    if (a.experts > kRouteMaxExperts) return false;
+    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)a.tokens), dim3(kRouteThreads), 0, st, a.logits, a.experts,
+                       (int)a.topk, a.renorm, a.ids, a.weights);
     return true;
 }
 
