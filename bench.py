@@ -16,7 +16,8 @@ carries: the roofline of the dominant kernel (the gate/up GEMV: a graph of
 back-to-back launches over the 64 distinct copies, timed with HIP events on
 the launch stream), the batch-4 step, the MoE GEMV (128-expert bank, top-8,
 1/2/4 tokens), the fused MoE decode block (routing, gate/up, SwiGLU, down and
-the weighted combine, same bank), the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
+the weighted combine, same bank), the expert-batched MoE prefill GEMM (a
+512-token prompt through the same bank), the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
 fraction, a plain copy kernel for reference, and the CPU oracle timed on a
 bounded sample (cpu_baseline).
 
@@ -54,7 +55,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=LAYERS)
-    p.add_argument("--only", default="", help="comma list of parts: dense,moe,moe_block,formats,gemm,copy,cpu")
+    p.add_argument("--only", default="", help="comma list of parts: dense,moe,moe_block,formats,gemm,moe_gemm,copy,cpu")
     p.add_argument("--profile-kernel", default="", help="run one kernel eagerly for rocprofv3")
     return p.parse_args()
 
@@ -96,7 +97,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    all_parts = {"dense", "moe", "moe_block", "formats", "gemm", "copy", "cpu"}
+    all_parts = {"dense", "moe", "moe_block", "formats", "gemm", "moe_gemm", "copy", "cpu"}
     parts = set(args.only.split(",")) if args.only else all_parts
 
     def u8(a):
@@ -327,6 +328,32 @@ def main():
         log(f"gemm: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
         del codes, scales, X, Y
         torch.cuda.empty_cache()
+
+    # ---------------- expert-batched MoE prefill GEMM ----------------
+    if "moe_gemm" in parts:
+        mg = {}
+        P = 512  # prompt tokens
+        for which in ("gate_up", "down"):
+            case = synth.moe_layer(which, 1, seed=0)
+            codes, scales = u8(case["codes"]), u8(case["scales"])
+            n, k = case["n"], case["k"]
+            _, _, sx, si, _ = synth.streams(300)
+            ids = torch.from_numpy(synth.moe_ids(si, P, 8, 128)).to(dev)
+            per = 1 if which == "down" else 0
+            x = bf(synth.bf16_normal(sx, (P, 8, k) if per else (P, k)))
+            y = torch.empty((P, 8, n), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty((128 + 1 + P * 8,), dtype=torch.int32, device=dev)
+            ms = timed_graph(lambda: mxq.moe_gemm(1, codes, scales, ids, x, per, out=y, workspace=ws), 10)
+            flops = 2.0 * P * 8 * n * k
+            tf = flops / (ms * 1e-3) / 1e12
+            mg[which] = dict(us=round(ms * 1e3, 2), tflops=round(tf, 1), mfma_peak_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+            log(f"moe gemm {which} {P} tokens x top-8: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+            del codes, scales
+            torch.cuda.empty_cache()
+        t_layer = (mg["gate_up"]["us"] + mg["down"]["us"]) * 1e-6
+        mg["layer"] = dict(us=round(t_layer * 1e6, 2), prefill_tok_s=round(P / (MOE_LAYERS * t_layer), 1),
+                           note=f"{P}-token prompt, expert FFN of {MOE_LAYERS} layers (gate/up + down GEMMs only)")
+        extras["moe_prefill_gemm"] = mg
 
     # ---------------- plain copy kernel for reference ----------------
     if "copy" in parts:

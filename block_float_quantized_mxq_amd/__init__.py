@@ -52,7 +52,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
-        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block):
+        L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
+        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
+                  L.mxq_moe_gemm):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -241,6 +243,42 @@ def gemm(fmt, codes, scales, x, global_scale=None, out_dtype=torch.bfloat16, out
     ydt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     _check(lib().mxq_gemm(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x), _ptr(out), ydt, m, n, k,
                           _stream(stream)), "mxq_gemm")
+    return out
+
+
+def moe_gemm(fmt, codes, scales, expert_ids, x, x_per_slot=0, global_scale=None, out_dtype=torch.bfloat16, out=None,
+             workspace=None, stream=None):
+    """Expert-batched MoE GEMM: y[t][s][i] = sum_k W[ids[t][s]][i][k] * x_ts[k] -> [m, topk, n] in float32 or
+    bfloat16 (RNE); x_ts = x[t] ([m, k]) or x[t][s] ([m, topk, k], x_per_slot).  workspace: int32
+    [experts + 1 + m * topk] (allocated when None)."""
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    expert_ids = _dev(expert_ids, torch.int32, "expert_ids")
+    x = _dev(x, torch.bfloat16, "x")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    experts, n = codes.shape[0], codes.shape[1]
+    k = _check_weight(fmt, codes, scales, global_scale, experts=experts)
+    if expert_ids.dim() != 2:
+        raise ValueError("expert_ids must be [m, topk]")
+    m, topk = expert_ids.shape
+    want = (m, topk, k) if x_per_slot else (m, k)
+    if tuple(x.shape) != want:
+        raise ValueError(f"x must have shape {want}, got {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty((m, topk, n), dtype=out_dtype, device=codes.device)
+    out = _dev(out, out_dtype, "out")
+    if out.numel() != m * topk * n:
+        raise ValueError("out must hold m * topk * n elements")
+    if workspace is None:
+        workspace = torch.empty((experts + 1 + m * topk,), dtype=torch.int32, device=codes.device)
+    workspace = _dev(workspace, torch.int32, "workspace")
+    if workspace.numel() < experts + 1 + m * topk:
+        raise ValueError("workspace must hold experts + 1 + m * topk int32")
+    ydt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    _check(lib().mxq_moe_gemm(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(expert_ids), _ptr(x),
+                              1 if x_per_slot else 0, _ptr(out), ydt, _ptr(workspace), experts, m, n, k, topk,
+                              _stream(stream)),
+           "mxq_moe_gemm")
     return out
 
 

@@ -206,6 +206,28 @@ MXQ_API mxq_status_t mxq_moe_route(const float* logits, int32_t* expert_ids, flo
     return launched(mxq::launch_moe_route(a, as_stream(stream)));
 }
 
+MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                  const int32_t* expert_ids, const uint16_t* x, int x_per_slot, void* y,
+                                  int y_dtype, int32_t* workspace, int64_t num_experts, int64_t m, int64_t n,
+                                  int64_t k, int64_t topk, void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (y_dtype != MXQ_OUT_F32 && y_dtype != MXQ_OUT_BF16) return MXQ_E_FORMAT;
+    if (!expert_ids || !x || !y || !workspace) return MXQ_E_NULLPTR;
+    if (num_experts <= 0 || m <= 0 || n <= 0 || k <= 0 || topk <= 0 || k % 32 != 0) return MXQ_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4) ||
+        !aligned(expert_ids, 4) || !aligned(workspace, 4))
+        return MXQ_E_ALIGN;
+    if (topk > MXQ_MAX_TOPK || num_experts > mxq::kMaxGroupExperts || m * topk > (int64_t(1) << 24) ||
+        n > kMaxDim || k > kMaxDim || mxq::moe_gemm_x_lds(k) > mxq::kMoeGemmMaxXLds)
+        return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::MoeGemmArgs a{fmt, codes, scales, global_scale, expert_ids, x, x_per_slot ? 1 : 0, y,
+                             y_dtype == MXQ_OUT_BF16 ? 1 : 0, workspace, num_experts, m, n, k, topk};
+    return launched(mxq::launch_moe_gemm(a, as_stream(stream)));
+}
+
 MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
                                    const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
                                    const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h,

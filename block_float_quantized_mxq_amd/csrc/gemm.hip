@@ -49,13 +49,6 @@ constexpr int kXStride = kBK + 8;                         // bf16 elements per L
 constexpr int kXTileElems = kBM * kXStride;               // per buffer
 constexpr int kXPieces = kBM * kBK / 8 / kGemmThreads;    // 16-byte X pieces per thread per slice
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);  // quiet NaN
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 // Tile coordinates of workgroup b (XCD-aware grouped order): consecutive
 // "local" indices of one XCD walk a GM-tall column strip of tiles, n fastest.
 __device__ __forceinline__ void tile_of(int64_t b, int64_t mt, int64_t nt, int64_t& tm, int64_t& tn) {

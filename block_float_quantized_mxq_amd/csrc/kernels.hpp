@@ -101,7 +101,30 @@ struct MoeBlockArgs {
 // power of two, dff bf16 each).
 constexpr int64_t kMoeBlockMaxLds = 64 * 1024;
 
+// Expert-batched MoE GEMM: Y[q][:] = W[ids[q]] . X[q / topk] (or X[q] with
+// x_per_slot) for the pairs q = token * topk + slot; workspace = goff[experts
+// + 1] then gperm[m * topk].
+struct MoeGemmArgs {
+    int fmt;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const float* gscale;
+    const int32_t* ids;
+    const uint16_t* x;
+    int x_per_slot;
+    void* y;
+    int y_bf16;
+    int32_t* workspace;
+    int64_t experts, m, n, k, topk;
+};
+constexpr int kMaxGroupExperts = 1024;
+// LDS of the gathered inputs of one block of 16 pairs (bf16 rows padded by 8
+// elements), and its budget: k up to 4088.
+constexpr int64_t moe_gemm_x_lds(int64_t k) { return 16 * (k + 8) * 2; }
+constexpr int64_t kMoeGemmMaxXLds = 128 * 1024;
+
 bool launch_moe_route(const RouteArgs& a, hipStream_t st);
+bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st);
 bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st);
 bool launch_dequant(const DequantArgs& a, hipStream_t st);
 bool launch_gemm(const GemmArgs& a, hipStream_t st);

@@ -204,6 +204,35 @@ mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_s
                            int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk,
                            void *stream);
 
+/*
+ * Expert-batched MoE GEMM (prefill).  The "Decoding block-float formats in
+ * software" section of the "MLxcel 0.8 release" post credits a kernel that
+ * processes the tokens expert by expert for its MXFP4 MoE prefill gain; here
+ * the routed (token, slot) pairs are grouped by expert on the GPU and each
+ * expert's weights are decoded to bf16 and multiplied on the matrix unit with
+ * its pairs' inputs, 16 pairs at a time (fp32 accumulate):
+ *
+ *   y[t][s][i] = sum_k W[expert_ids[t][s]][i][k] * x_ts[k]
+ *   x_ts = x[t] (x_per_slot == 0, e.g. gate/up) or x[t][s] (x_per_slot != 0, e.g. down)
+ *
+ *   codes/scales   bank [num_experts][n][...] (layout as mxq_moe_gemv)
+ *   global_scale   NVFP4: fp32 [num_experts]; MX: NULL
+ *   expert_ids     int32 [m][topk]; x bf16 [m][k] or [m][topk][k]
+ *   y              [m][topk][n], bf16 (RNE of the fp32 value) or fp32 (y_dtype)
+ *   workspace      int32 [num_experts + 1 + m * topk], caller-owned, 4-byte
+ *                  aligned: per-expert offsets, then the grouped pair order
+ *   m 1 .. 2^24 / topk;  topk 1 .. MXQ_MAX_TOPK;  num_experts 1 .. 1024;
+ *   n >= 1;  k a positive multiple of 32, at most 4088 (the inputs of 16 pairs
+ *   are staged in 128 KiB of LDS; larger k gives MXQ_E_UNSUPPORTED)
+ * A pair whose id is outside [0, num_experts) gets a NaN output row.  Two
+ * kernels run on `stream` (grouping, then the GEMM); the workspace must not be
+ * shared by calls that overlap.
+ */
+mxq_status_t mxq_moe_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                          const int32_t *expert_ids, const uint16_t *x, int x_per_slot, void *y, int y_dtype,
+                          int32_t *workspace, int64_t num_experts, int64_t m, int64_t n, int64_t k, int64_t topk,
+                          void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 

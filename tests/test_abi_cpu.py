@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
-         "mxq_status_string", "mxq_abi_version"])
+         "mxq_moe_gemm", "mxq_status_string", "mxq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -70,7 +70,11 @@ def block(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=None, 
                                    E, hidden, dff, T, topk, None)
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block])
+def mgemm(fmt=1, codes=A, scales=A, g=None, ids=A, x=A, per=0, y=A, ydt=0, ws=A, E=4, m=3, n=8, k=64, topk=2):
+    return mxq.lib().mxq_moe_gemm(fmt, codes, scales, g, ids, x, per, y, ydt, ws, E, m, n, k, topk, None)
+
+
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, mgemm])
 def test_format_errors(call):
     assert call(fmt=0) == FORMAT
     assert call(fmt=4) == FORMAT
@@ -79,7 +83,7 @@ def test_format_errors(call):
     assert call(fmt=2, g=A) == FORMAT
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block])
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, mgemm])
 def test_null_pointers(call):
     assert call(codes=None) == NULLPTR
     assert call(scales=None) == NULLPTR
@@ -93,6 +97,8 @@ def test_null_pointers_per_entry():
     assert route(logits=None) == NULLPTR and route(ids=None) == NULLPTR and route(w=None) == NULLPTR
     for arg in ("dn_codes", "dn_scales", "ids", "w", "x", "h", "y"):
         assert block(**{arg: None}) == NULLPTR, arg
+    for arg in ("ids", "x", "y", "ws"):
+        assert mgemm(**{arg: None}) == NULLPTR, arg
 
 
 def test_shape_errors():
@@ -115,6 +121,11 @@ def test_shape_errors():
     assert block(fmt=3, g=A, dn_g=A, dff=40) == SHAPE
     # the two banks of one block share the format: its per-tensor scales go with it
     assert block(fmt=3, g=A, dn_g=None) == FORMAT and block(fmt=1, dn_g=A) == FORMAT
+    for bad in (0, -1):
+        for arg in ("E", "m", "n", "k", "topk"):
+            assert mgemm(**{arg: bad}) == SHAPE, arg
+    assert mgemm(k=48) == SHAPE and mgemm(fmt=3, g=A, k=16) == SHAPE  # whole 32-element blocks
+    assert mgemm(ydt=2) == FORMAT
 
 
 def test_alignment_errors():
@@ -127,6 +138,8 @@ def test_alignment_errors():
     for arg, off in (("codes", 8), ("dn_codes", 4), ("x", 8), ("h", 4), ("y", 2), ("ids", 2), ("w", 1)):
         assert block(**{arg: A + off}) == ALIGN, arg
     assert block(fmt=3, g=A, dn_g=A + 2) == ALIGN
+    for arg, off in (("codes", 8), ("x", 8), ("y", 2), ("ids", 2), ("ws", 1)):
+        assert mgemm(**{arg: A + off}) == ALIGN, arg
 
 
 def test_unsupported_sizes():
@@ -139,6 +152,9 @@ def test_unsupported_sizes():
     # activations of the padded slot count staged in 64 KiB of LDS: 8 slots x 4096 x 2 bytes fit, 4128 do not
     assert block(topk=8, dff=4128) == UNSUPPORTED and block(topk=5, dff=4128) == UNSUPPORTED
     assert block(topk=4, dff=8224) == UNSUPPORTED and block(topk=2, dff=16416) == UNSUPPORTED
+    assert mgemm(topk=17) == UNSUPPORTED and mgemm(E=1025) == UNSUPPORTED
+    assert mgemm(m=(1 << 24) // 8 + 1, topk=8) == UNSUPPORTED and mgemm(n=1 << 31) == UNSUPPORTED
+    assert mgemm(k=4096) == UNSUPPORTED  # 16 padded input rows must fit 128 KiB of LDS
 
 
 def _no_gpu():
@@ -149,7 +165,8 @@ def _no_gpu():
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is present (it would launch on fake pointers)")
 def test_device_error_without_gpu():
     assert gemv() == DEVICE and moe() == DEVICE and gemm() == DEVICE and deq() == DEVICE
-    assert route() == DEVICE and block() == DEVICE
+    assert route() == DEVICE and block() == DEVICE and mgemm() == DEVICE
+    assert mgemm(m=(1 << 24) // 8, topk=8, E=1024, k=4064) == DEVICE  # largest accepted sizes
     assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
 
