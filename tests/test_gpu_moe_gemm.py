@@ -129,7 +129,8 @@ def test_30b_a3b_prefill_sampled(which):
 @pytest.mark.parametrize("k", [32, 96, 768, 1024, 1280, 2048, 2560, 3072, 4064])
 def test_register_tile_variants(fmt, k):
     """Row lengths that select every (k split, register blocks per lane) variant
-    of the per-expert kernel, including ranges that end inside a lane's blocks;
-    every output checked."""
+    of the per-expert kernel -- 1 x 4 (k <= 512), 1 x 6 (768), 1 x 8 (1024),
+    2 x 6 (1280), 2 x 8 (2048), 4 x 6 (2560, 3072), 4 x 8 (4064) -- including
+    ranges that end inside a lane's blocks; every output checked."""
     c = case(fmt, 8, 40, k, 21, 3, 140 + k + fmt)
     check(c, f"moe gemm variants {FMT_NAMES[fmt]} k={k}")
