@@ -69,6 +69,7 @@ def _load():
         lib.orc_round_bf16.restype = ctypes.c_double
         D = ctypes.c_double
         lib.orc_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, D, D, D, P, P, P]
+        lib.orc_quantize.argtypes = [I, P, ctypes.c_float, I64, I64, P, P]
         _lib = lib
     return _lib
 
@@ -206,6 +207,17 @@ def moe_block(fmt, gu_codes, gu_scales, gu_g, dn_codes, dn_scales, dn_g, ids, w,
                           _ptr(dn_g), _ptr(ids), _ptr(w), _ptr(x), experts, hidden, dff, tokens, topk,
                           h_rel, h_abs, p_rel, _ptr(y), _ptr(a), _ptr(amb))
     return (y, a) if amb is None else (y, a, amb)
+
+
+def quantize(fmt, x, g, rows, k):
+    """(codes, scales) of bf16 bits x [rows][k] (uint16): MX blocks of 32 with E8M0 scales
+    (OCP MX conversion), NVFP4 blocks of 16 with E4M3 scales for the per-tensor scale g."""
+    _check(fmt, k)
+    x = _c(x, np.uint16)
+    codes = np.zeros((rows, k if fmt == 2 else k // 2), dtype=np.uint8)
+    scales = np.zeros((rows, k // (16 if fmt == 3 else 32)), dtype=np.uint8)
+    _load().orc_quantize(fmt, _ptr(x), float(g if g is not None else 1.0), rows, k, _ptr(codes), _ptr(scales))
+    return codes, scales
 
 
 def within_tolerance(y_gpu, y_ref, abs_ref, rel=1e-5, atol=1e-6):

@@ -387,3 +387,114 @@ void orc_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales, c
         free(a);
     }
 }
+
+/* ---- block-float quantizer: bf16 -> MXFP4 / MXFP8 / NVFP4 ----------------------
+ *
+ * The ROCm status table of the "Build from source" manual (section "Current
+ * status", row "mxfp8, mxfp4 checkpoints") requantizes vendor FP8 block
+ * checkpoints to MXFP8 when a model is loaded.  The pages give no procedure;
+ * the reading taken here is the OCP MX v1.0 conversion and, for NVFP4, a block
+ * scale that maps the block maximum onto the largest E2M1 value:
+ *
+ *   MX (32-element blocks):  amax = max |v|;  X = 2^(floor(log2 amax) - emax),
+ *        emax = 2 (E2M1, largest value 6) or 8 (E4M3, largest 448); the
+ *        exponent is clamped to [-127, 127] (amax = 0 takes -127) and stored
+ *        as the E8M0 byte exponent + 127.  Element code = q(v / X).
+ *   NVFP4 (16-element blocks, caller's per-tensor fp32 scale g > 0):
+ *        t = fl32(amax / fl32(6 g));  s = e4m3(t) (rounded as below);
+ *        element code = q(fl32(v / fl32(s g))), or +-0 when s = 0.
+ *   q(p): the sign of p, and |p| rounded to the element format's nearest value,
+ *        ties to the even code (last mantissa bit 0), values above the largest
+ *        one saturating to it.  With e = max(floor(log2 |p|), emin) the spacing
+ *        of representable values near |p| is 2^(e - mbits); E2M1: mbits 1,
+ *        emin 0, max 6; E4M3: mbits 3, emin -6, max 448.
+ * Inputs must be finite. */
+
+/* |p| rounded to the grid (mbits, emin), saturating at maxv; a >= 0. */
+static double orc_quant_mag(double a, int mbits, int emin, double maxv)
+{
+    if (a == 0.0) return 0.0;
+    if (a >= maxv) return maxv; /* saturate (also an fp32 quotient that overflowed) */
+    int e;
+    (void)frexp(a, &e);
+    e -= 1; /* floor(log2 a) */
+    if (e < emin) e = emin;
+    const double q = ldexp(1.0, e - mbits);
+    const double r = nearbyint(a / q) * q; /* round to nearest, ties to even */
+    return r > maxv ? maxv : r;
+}
+
+/* code of a representable magnitude r (sign bit clear) */
+static unsigned orc_e2m1_code(double r)
+{
+    static const double v[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    for (unsigned c = 0; c < 8; ++c)
+        if (v[c] == r) return c;
+    return 0xFFu; /* not reached for rounded magnitudes */
+}
+
+static unsigned orc_e4m3_code(double r)
+{
+    if (r < ldexp(1.0, -6)) return (unsigned)(r / ldexp(1.0, -9)); /* subnormal: e = 0 */
+    int e;
+    (void)frexp(r, &e);
+    e -= 1;
+    const unsigned m = (unsigned)((r / ldexp(1.0, e) - 1.0) * 8.0);
+    return ((unsigned)(e + 7) << 3) | m;
+}
+
+void orc_quantize(int fmt, const uint16_t *x, float g, int64_t rows, int64_t k, uint8_t *codes, uint8_t *scales)
+{
+    const int bs = orc_block(fmt);
+    const int64_t nb = k / bs;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + r * k + b * bs;
+            double amax = 0.0;
+            for (int j = 0; j < bs; ++j) {
+                const double a = fabs(orc_bf16(xb[j]));
+                if (a > amax) amax = a;
+            }
+            double div = 1.0; /* p = v / div */
+            int zero = 0;
+            if (fmt == ORC_NVFP4) {
+                const float t = (float)amax / (6.0f * g);
+                const double s = orc_quant_mag((double)t, 3, -6, 448.0);
+                scales[r * nb + b] = (uint8_t)orc_e4m3_code(s);
+                zero = (s == 0.0);
+                div = (double)((float)s * g);
+            } else {
+                const int emax = fmt == ORC_MXFP4 ? 2 : 8;
+                int se = -127;
+                if (amax > 0.0) {
+                    int e;
+                    (void)frexp(amax, &e);
+                    se = (e - 1) - emax;
+                    if (se < -127) se = -127;
+                    if (se > 127) se = 127;
+                }
+                scales[r * nb + b] = (uint8_t)(se + 127);
+                div = ldexp(1.0, se);
+            }
+            for (int j = 0; j < bs; ++j) {
+                const double v = orc_bf16(xb[j]);
+                const unsigned neg = (xb[j] >> 15) & 1u;
+                double p;
+                if (fmt == ORC_NVFP4) p = zero ? 0.0 : (double)((float)v / (float)div); /* fp32 division */
+                else p = v / div;                                                     /* exact: div = 2^se */
+                unsigned c;
+                if (fmt == ORC_MXFP8) c = orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)) | (neg << 7);
+                else c = orc_e2m1_code(orc_quant_mag(fabs(p), 1, 0, 6.0)) | (neg << 3);
+                const int64_t kk = b * bs + j;
+                if (fmt == ORC_MXFP8) {
+                    codes[r * k + kk] = (uint8_t)c;
+                } else {
+                    uint8_t *byte = &codes[r * (k / 2) + kk / 2];
+                    if (kk % 2 == 0) *byte = (uint8_t)((*byte & 0xF0u) | c);
+                    else *byte = (uint8_t)((*byte & 0x0Fu) | (c << 4));
+                }
+            }
+        }
+    }
+}

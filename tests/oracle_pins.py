@@ -442,6 +442,136 @@ def check_block_rounding_bound():
             assert np.median(amb / a) < 1e-7
 
 
+# ---- block-float quantizer ---------------------------------------------------------------
+# An independent reference: element values from the stored E2M1 table and torch's E4M3
+# decoder, the nearest value found by exhaustive search (ties: even code), the MX scale
+# exponent from math.frexp, the NVFP4 arithmetic in numpy float32.
+
+def _grid(fmt_elem):
+    """[(value, code)] of the non-negative finite codes of E2M1 ("e2m1") or E4M3 ("e4m3")."""
+    if fmt_elem == "e2m1":
+        table = bf.e2m1_table()
+        return [(table[c], c) for c in range(8)]
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().tolist()
+    return [(v, c) for c, v in enumerate(vals)]
+
+
+def _nearest(a, grid):
+    """Code of the grid value nearest to a >= 0; ties to the even code; above the top: the top."""
+    top = max(grid)
+    if a >= top[0]:
+        return top[1]
+    best = None
+    for v, c in grid:
+        d = abs(v - a)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def _quantize_reference(fmt, xbits, g):
+    f = torch.from_numpy(xbits.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    rows, k = f.shape
+    bs = 16 if fmt == NVFP4 else 32
+    e2m1, e4m3 = _grid("e2m1"), _grid("e4m3")
+    codes = np.zeros((rows, k), dtype=np.int64)
+    scales = np.zeros((rows, k // bs), dtype=np.uint8)
+    for r in range(rows):
+        for b in range(k // bs):
+            blk = f[r, b * bs:(b + 1) * bs]
+            amax = float(np.max(np.abs(blk)))
+            if fmt == NVFP4:
+                t = float(np.float32(amax) / (np.float32(6.0) * np.float32(g)))
+                sc = _nearest(t, e4m3)
+                scales[r, b] = sc
+                s_val = dict((c, v) for v, c in e4m3)[sc]
+                den = np.float32(np.float32(s_val) * np.float32(g))
+                with np.errstate(over="ignore"):  # an overflowing quotient saturates
+                    ps = [0.0 if s_val == 0 else float(np.float32(v) / den) for v in blk]
+            else:
+                emax = 2 if fmt == MXFP4 else 8
+                se = -127 if amax == 0 else min(127, max(-127, math.frexp(amax)[1] - 1 - emax))
+                scales[r, b] = se + 127
+                ps = [v / 2.0 ** se for v in blk]
+            for j, pv in enumerate(ps):
+                neg = int(xbits[r, b * bs + j]) >> 15
+                if fmt == MXFP8:
+                    codes[r, b * bs + j] = _nearest(abs(pv), e4m3) | (neg << 7)
+                else:
+                    codes[r, b * bs + j] = _nearest(abs(pv), e2m1) | (neg << 3)
+    if fmt != MXFP8:
+        codes = (codes[:, 0::2] | (codes[:, 1::2] << 4))
+    return codes.astype(np.uint8), scales
+
+
+def _bits(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _quant_cases(fmt, seed):
+    rng = np.random.default_rng(seed)
+    bs = 16 if fmt == NVFP4 else 32
+    rows = []
+    # random magnitudes spread over many binades, both signs
+    for _ in range(6):
+        rows.append((rng.standard_normal(2 * bs) * np.exp2(rng.integers(-20, 20, size=2 * bs))).tolist())
+    # exact ties of the element grids, with the block maximum fixing the scale
+    if fmt == MXFP8:
+        ties = [256.0, 1.0625, 1.1875, 3.0 * 2 ** -10, 2 ** -10, -1.0625, 0.0, -0.0, 300.0, 2 ** -11]
+    else:
+        ties = [5.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, -0.25, -5.0, 0.0, -0.0, 0.1, 4.9]
+    rows.append((ties * (2 * bs // len(ties) + 1))[:2 * bs])
+    rows.append([0.0] * (2 * bs))                                       # zero blocks
+    rows.append([1e-39, -2e-40] + [0.0] * (2 * bs - 2))                 # bf16 subnormals: scale clamp
+    rows.append([3.0e38] + [1.0] * (2 * bs - 1))                        # near the top of bf16
+    return _bits(rows)
+
+
+def check_quantize_nearest(fmt):
+    x = _quant_cases(fmt, 7 + fmt)
+    g = float(np.float32(1.0 / 2688.0)) if fmt == NVFP4 else None
+    rows, k = x.shape
+    for gg in ([g, float(np.float32(0.75)), float(np.float32(3.0e-3))] if fmt == NVFP4 else [None]):
+        codes, scales = oracle.quantize(fmt, x, gg, rows, k)
+        rc, rs = _quantize_reference(fmt, x, gg)
+        assert (scales == rs).all(), (fmt, gg, np.argwhere(scales != rs)[:3])
+        assert (codes == rc).all(), (fmt, gg, np.argwhere(codes != rc)[:3])
+
+
+def check_quantize_scale_closed_form():
+    one = _bits([[1.0] * 32])
+    assert oracle.quantize(MXFP4, one, None, 1, 32)[1][0, 0] == 127 - 2     # 1 = 2^0, emax 2
+    assert oracle.quantize(MXFP8, one, None, 1, 32)[1][0, 0] == 127 - 8     # emax 8
+    six = _bits([[6.0] + [0.0] * 31])
+    assert oracle.quantize(MXFP4, six, None, 1, 32)[1][0, 0] == 127         # 6 in [4, 8): 2^(2-2)
+    assert oracle.quantize(MXFP4, six, None, 1, 32)[0][0, 0] == 0x07        # code of 6
+    zero = _bits([[0.0] * 32])
+    assert oracle.quantize(MXFP4, zero, None, 1, 32)[1][0, 0] == 0           # exponent clamped to -127
+    tiny = _bits([[2.0 ** -133] + [0.0] * 31])                               # smallest bf16 subnormal
+    assert oracle.quantize(MXFP8, tiny, None, 1, 32)[1][0, 0] == 0
+
+
+def check_quantize_roundtrip(fmt, seed=17):
+    """Blocks whose largest code is 4 or 6 (E2M1) / has exponent field 15 (E4M3): the
+    dequantized bf16 weights quantize back to the same codes and scales."""
+    rng = np.random.default_rng(seed)
+    n, k = 24, 128
+    codes, scales, _, _ = _rand_case(fmt, rng, n, k, 100, 150)
+    if fmt == MXFP4:
+        nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(n, k)
+        nib[:, ::32] = rng.choice([6, 7, 14, 15], size=(n, k // 32))      # one +-4 or +-6 per block
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    else:
+        codes[:, ::32] = rng.choice([0x78, 0x7B, 0x7E, 0xF8, 0xFE], size=(n, k // 32))
+    w = oracle.dequant(fmt, codes, scales, None, n, k)
+    xb = torch.from_numpy(w).to(torch.bfloat16)
+    assert torch.equal(xb.float(), torch.from_numpy(w)), "decoded weights are bf16 values"
+    x = xb.view(torch.int16).numpy().view(np.uint16)
+    qc, qs = oracle.quantize(fmt, x, None, n, k)
+    assert (qs == scales).all()
+    assert (qc == codes).all()
+
+
 def all_checks():
     """(name, callable) for every pin, used by the mutation test."""
     out = [("e2m1_table", check_e2m1_table), ("e8m0", check_e8m0), ("e4m3", check_e4m3),
@@ -457,4 +587,8 @@ def all_checks():
                 (f"moe_block_{f}", lambda f=f: check_moe_block(f))]
     out += [("route", check_route), ("silu", check_silu), ("round_bf16", check_round_bf16),
             ("swiglu_tie", check_swiglu_tie), ("block_rounding_bound", check_block_rounding_bound)]
+    out += [(f"quantize_nearest_{f}", lambda f=f: check_quantize_nearest(f)) for f in FMTS]
+    out += [("quantize_scale_closed_form", check_quantize_scale_closed_form),
+            ("quantize_roundtrip_mxfp4", lambda: check_quantize_roundtrip(MXFP4)),
+            ("quantize_roundtrip_mxfp8", lambda: check_quantize_roundtrip(MXFP8))]
     return out

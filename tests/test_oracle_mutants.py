@@ -15,6 +15,12 @@ import oracle_pins as pins  # noqa: E402
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
+    "quant_emax_fp4": ("const int emax = fmt == ORC_MXFP4 ? 2 : 8;", "const int emax = fmt == ORC_MXFP4 ? 3 : 8;"),
+    "quant_emax_fp8": ("const int emax = fmt == ORC_MXFP4 ? 2 : 8;", "const int emax = fmt == ORC_MXFP4 ? 2 : 7;"),
+    "quant_truncate": ("const double r = nearbyint(a / q) * q;", "const double r = floor(a / q) * q;"),
+    "quant_ties_away": ("const double r = nearbyint(a / q) * q;", "const double r = round(a / q) * q;"),
+    "quant_sign_dropped": ("| (neg << 3);", ";"),
+    "quant_nv_scale_target": ("(float)amax / (6.0f * g);", "(float)amax / (4.0f * g);"),
     "nibble_order": ("(k % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4)", "(k % 2 == 1) ? (byte & 0x0Fu) : (byte >> 4)"),
     "e2m1_bias": ("ldexp(1.0 + 0.5 * (double)m, (int)e - 1)", "ldexp(1.0 + 0.5 * (double)m, (int)e - 2)"),
     "e2m1_subnormal": ("0.5 * (double)m :", "1.0 * (double)m :"),
@@ -66,7 +72,7 @@ def test_pins_reject_mutant(tmp_path, monkeypatch, name):
     mutant = ctypes.CDLL(path)
     for attr in ("orc_e2m1", "orc_e8m0", "orc_e4m3", "orc_bf16", "orc_num_threads", "orc_set_num_threads",
                  "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows", "orc_moe_route", "orc_silu",
-                 "orc_round_bf16", "orc_moe_block"):
+                 "orc_round_bf16", "orc_moe_block", "orc_quantize"):
         fr, fm = getattr(real, attr), getattr(mutant, attr)
         fm.argtypes, fm.restype = fr.argtypes, fr.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
