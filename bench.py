@@ -17,7 +17,8 @@ back-to-back launches over the 64 distinct copies, timed with HIP events on
 the launch stream), the batch-4 step, the MoE GEMV (128-expert bank, top-8,
 1/2/4 tokens), the fused MoE decode block (routing, gate/up, SwiGLU, down and
 the weighted combine, same bank), the expert-batched MoE prefill GEMM (a
-512-token prompt through the same bank), the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
+512-token prompt through the same bank), the block-float quantizer on a
+51200 x 5120 bf16 matrix, the MXFP8 / NVFP4 format sweep, the prefill GEMM's MFMA-peak
 fraction, a plain copy kernel for reference, and the CPU oracle timed on a
 bounded sample (cpu_baseline).
 
@@ -55,7 +56,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=LAYERS)
-    p.add_argument("--only", default="", help="comma list of parts: dense,moe,moe_block,formats,gemm,moe_gemm,copy,cpu")
+    p.add_argument("--only", default="", help="comma list of parts: dense,moe,moe_block,formats,gemm,moe_gemm,quantize,copy,cpu")
     p.add_argument("--profile-kernel", default="", help="run one kernel eagerly for rocprofv3")
     return p.parse_args()
 
@@ -97,7 +98,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    all_parts = {"dense", "moe", "moe_block", "formats", "gemm", "moe_gemm", "copy", "cpu"}
+    all_parts = {"dense", "moe", "moe_block", "formats", "gemm", "moe_gemm", "quantize", "copy", "cpu"}
     parts = set(args.only.split(",")) if args.only else all_parts
 
     def u8(a):
@@ -354,6 +355,23 @@ def main():
         mg["layer"] = dict(us=round(t_layer * 1e6, 2), prefill_tok_s=round(P / (MOE_LAYERS * t_layer), 1),
                            note=f"{P}-token prompt, expert FFN of {MOE_LAYERS} layers (gate/up + down GEMMs only)")
         extras["moe_prefill_gemm"] = mg
+
+    # ---------------- block-float quantizer ----------------
+    if "quantize" in parts:
+        qz = {}
+        rows, k = 51200, 5120
+        xq = torch.randn(rows, k, device=dev, generator=torch.Generator(device=dev).manual_seed(0)).to(torch.bfloat16)
+        gq = torch.tensor([1.0 / 2688.0], dtype=torch.float32, device=dev)
+        for fmt, name in ((mxq.MXFP4, "mxfp4"), (mxq.MXFP8, "mxfp8"), (mxq.NVFP4, "nvfp4")):
+            cq, sq = mxq.quantize(fmt, xq, gq if fmt == mxq.NVFP4 else None)
+            ms = timed_graph(lambda: mxq.quantize(fmt, xq, gq if fmt == mxq.NVFP4 else None, codes=cq, scales=sq), 10)
+            byts = rows * k * 2 + mxq.weight_bytes(fmt, rows, k)
+            qz[name] = dict(us=round(ms * 1e3, 2), gbs=round(byts / (ms * 1e-3) / 1e9, 1),
+                            pct_peak=round(100 * byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2), bytes=byts)
+            log(f"quantize {name} {rows}x{k}: {ms * 1e3:.1f} us, {qz[name]['gbs']:.0f} GB/s (bf16 in + codes/scales out)")
+        del xq
+        torch.cuda.empty_cache()
+        extras["quantize_51200x5120"] = qz
 
     # ---------------- plain copy kernel for reference ----------------
     if "copy" in parts:

@@ -53,8 +53,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
+        L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
-                  L.mxq_moe_gemm):
+                  L.mxq_moe_gemm, L.mxq_quantize):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -280,6 +281,28 @@ def moe_gemm(fmt, codes, scales, expert_ids, x, x_per_slot=0, global_scale=None,
                               _stream(stream)),
            "mxq_moe_gemm")
     return out
+
+
+def quantize(fmt, x, global_scale=None, codes=None, scales=None, stream=None):
+    """bf16 x [rows, k] -> (codes uint8 [rows, k/2] or [rows, k], scales uint8 [rows, k/block]); NVFP4 takes its
+    per-tensor scale as a float32 [1] device tensor."""
+    x = _dev(x, torch.bfloat16, "x")
+    global_scale = _dev(global_scale, torch.float32, "global_scale")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, k]")
+    rows, k = x.shape
+    cb = k if fmt == MXFP8 else k // 2
+    if codes is None:
+        codes = torch.empty((rows, cb), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // BLOCK.get(fmt, 32)), dtype=torch.uint8, device=x.device)
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    if codes.numel() != rows * cb or scales.numel() != rows * (k // BLOCK.get(fmt, 32)):
+        raise ValueError("codes / scales do not match x")
+    _check(lib().mxq_quantize(fmt, _ptr(x), _ptr(global_scale), _ptr(codes), _ptr(scales), rows, k,
+                              _stream(stream)), "mxq_quantize")
+    return codes, scales
 
 
 def dequant(fmt, codes, scales, global_scale=None, out=None, stream=None):

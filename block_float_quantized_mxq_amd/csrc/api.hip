@@ -206,6 +206,22 @@ MXQ_API mxq_status_t mxq_moe_route(const float* logits, int32_t* expert_ids, flo
     return launched(mxq::launch_moe_route(a, as_stream(stream)));
 }
 
+MXQ_API mxq_status_t mxq_quantize(int fmt, const uint16_t* x, const float* global_scale, uint8_t* codes,
+                                  uint8_t* scales, int64_t rows, int64_t k, void* stream) {
+    if (fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4) return MXQ_E_FORMAT;
+    if ((fmt == MXQ_FMT_NVFP4) != (global_scale != nullptr)) return MXQ_E_FORMAT;
+    if (!x || !codes || !scales) return MXQ_E_NULLPTR;
+    if (rows <= 0) return MXQ_E_SHAPE;
+    mxq_status_t st;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
+    if (rows > kMaxDim || k > kMaxDim || rows * k > mxq::kMaxQuantizeElems) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::QuantizeArgs a{fmt, x, global_scale, codes, scales, rows, k};
+    return launched(mxq::launch_quantize(a, as_stream(stream)));
+}
+
 MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                                   const int32_t* expert_ids, const uint16_t* x, int x_per_slot, void* y,
                                   int y_dtype, int32_t* workspace, int64_t num_experts, int64_t m, int64_t n,

@@ -123,6 +123,18 @@ constexpr int kMaxGroupExperts = 1024;
 constexpr int64_t moe_gemm_x_lds(int64_t k) { return 16 * (k + 8) * 2; }
 constexpr int64_t kMoeGemmMaxXLds = 128 * 1024;
 
+// Quantizer: bf16 x[rows][k] -> codes and block scales (NVFP4: per-tensor scale gscale[0] given).
+struct QuantizeArgs {
+    int fmt;
+    const uint16_t* x;
+    const float* gscale;
+    uint8_t* codes;
+    uint8_t* scales;
+    int64_t rows, k;
+};
+constexpr int64_t kMaxQuantizeElems = int64_t(1) << 36;
+
+bool launch_quantize(const QuantizeArgs& a, hipStream_t st);
 bool launch_moe_route(const RouteArgs& a, hipStream_t st);
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st);
 bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st);

@@ -1,0 +1,133 @@
+// quantize.hip -- block-float quantizer: bf16 rows -> MXFP4 / MXFP8 / NVFP4
+// codes and block scales (the inverse of the decode the other kernels run).
+//
+// The ROCm status table of the "Build from source" manual (section "Current
+// status", row "mxfp8, mxfp4 checkpoints") requantizes vendor FP8 block
+// checkpoints to MXFP8 when a model is loaded.  The conversion follows OCP MX
+// v1.0: shared exponent floor(log2 amax) - emax (emax 2 for E2M1, 8 for
+// E4M3), clamped to [-127, 127], zero blocks at -127; NVFP4 takes the E4M3
+// block scale of amax / (6 g) for the caller's per-tensor scale g.  Elements
+// are rounded to the nearest value of the element format, ties to the even
+// code, saturating at its largest value; the input's sign is kept.
+//
+// One lane per block: it loads the block's bf16 values (64 or 32 bytes),
+// finds the maximum magnitude, picks the scale and writes the codes (16, 32 or
+// 8 bytes) and the scale byte.  Every step is an exact power-of-two scaling or
+// a round-to-nearest-even in fp32, plus, for NVFP4, two correctly rounded fp32
+// divisions; HBM bound (2 bytes read per element).
+#include "kernels.hpp"
+#include "mxq_device.hpp"
+#include "rows_core.hpp"
+
+namespace mxq {
+
+// |p| rounded to the grid of mbits mantissa bits and minimum exponent emin,
+// saturating at maxv (a >= 0).
+__device__ __forceinline__ float quant_mag(float a, int mbits, int emin, float maxv) {
+    if (a == 0.0f) return 0.0f;
+    if (a >= maxv) return maxv;
+    int e = __builtin_amdgcn_frexp_expf(a) - 1;  // floor(log2 a)
+    e = e < emin ? emin : e;
+    const float r = __builtin_rintf(__builtin_amdgcn_ldexpf(a, mbits - e));  // ties to even
+    const float v = __builtin_amdgcn_ldexpf(r, e - mbits);
+    return v > maxv ? maxv : v;
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float r) {  // r in {0, .5, 1, 1.5, 2, 3, 4, 6}
+    return r < 2.0f ? (uint32_t)(r * 2.0f) : (r < 4.0f ? (r == 3.0f ? 5u : 4u) : (r == 6.0f ? 7u : 6u));
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float r) {  // r a representable E4M3 magnitude
+    if (r < 0.015625f) return (uint32_t)(r * 512.0f);     // subnormal: multiples of 2^-9
+    const int e = __builtin_amdgcn_frexp_expf(r) - 1;
+    const uint32_t m = (uint32_t)(__builtin_amdgcn_ldexpf(r, -e) * 8.0f) - 8u;
+    return ((uint32_t)(e + 7) << 3) | m;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
+                                                       const float* __restrict__ gscale,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                       int64_t rows, int64_t k) {
+    constexpr int BS = BlockSize<FMT>::value;
+    const int64_t nb = k / BS;
+    const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blk >= rows * nb) return;
+    const int64_t r = blk / nb, b = blk % nb;
+
+    uint32_t w[BS / 2];  // bf16 pairs
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + r * k + b * BS);
+#pragma unroll
+    for (int i = 0; i < BS / 8; ++i) {
+        const u32x4_t v = src[i];
+        w[4 * i + 0] = v[0]; w[4 * i + 1] = v[1]; w[4 * i + 2] = v[2]; w[4 * i + 3] = v[3];
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BS / 2; ++i) {
+        const float lo = __builtin_fabsf(bf16_lo_to_f32(w[i])), hi = __builtin_fabsf(bf16_hi_to_f32(w[i]));
+        amax = lo > amax ? lo : amax;
+        amax = hi > amax ? hi : amax;
+    }
+
+    // p = v * mul (MX: mul = 2^-se, exact) or p = v / den (NVFP4)
+    float mul = 1.0f, den = 1.0f;
+    bool zero = false;
+    if constexpr (FMT == kNVFP4) {
+        const float g = gscale[0];
+        const float t = amax / (6.0f * g);
+        const float s = quant_mag(t, 3, -6, 448.0f);
+        scales[blk] = (uint8_t)e4m3_code(s);
+        zero = s == 0.0f;
+        den = s * g;
+    } else {
+        constexpr int emax = FMT == kMXFP4 ? 2 : 8;
+        int se = -127;
+        if (amax > 0.0f) {
+            se = __builtin_amdgcn_frexp_expf(amax) - 1 - emax;
+            se = se < -127 ? -127 : (se > 127 ? 127 : se);
+        }
+        scales[blk] = (uint8_t)(se + 127);
+        mul = __builtin_amdgcn_ldexpf(1.0f, -se);  // se >= -127: 2^127 at most, normal
+    }
+
+    uint32_t out[FMT == kMXFP8 ? BS / 4 : BS / 8] = {};
+#pragma unroll
+    for (int j = 0; j < BS; ++j) {
+        const uint32_t bits = (j & 1) ? (w[j / 2] >> 16) : (w[j / 2] & 0xFFFFu);
+        const float v = __builtin_bit_cast(float, bits << 16);
+        float p;
+        if constexpr (FMT == kNVFP4) p = zero ? 0.0f : v / den;
+        else p = v * mul;
+        const uint32_t neg = bits >> 15;
+        if constexpr (FMT == kMXFP8) {
+            const uint32_t c = e4m3_code(quant_mag(__builtin_fabsf(p), 3, -6, 448.0f)) | (neg << 7);
+            out[j / 4] |= c << (8 * (j % 4));
+        } else {
+            const uint32_t c = e2m1_code(quant_mag(__builtin_fabsf(p), 1, 0, 6.0f)) | (neg << 3);
+            out[j / 8] |= c << (4 * (j % 8));
+        }
+    }
+    if constexpr (FMT == kMXFP8) {
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(codes + r * k + b * BS);
+        dst[0] = u32x4_t{out[0], out[1], out[2], out[3]};
+        dst[1] = u32x4_t{out[4], out[5], out[6], out[7]};
+    } else if constexpr (FMT == kMXFP4) {
+        *reinterpret_cast<u32x4_t*>(codes + r * (k / 2) + b * 16) = u32x4_t{out[0], out[1], out[2], out[3]};
+    } else {
+        *reinterpret_cast<u32x2_t*>(codes + r * (k / 2) + b * 8) = u32x2_t{out[0], out[1]};
+    }
+}
+
+bool launch_quantize(const QuantizeArgs& a, hipStream_t st) {
+    const int64_t nb = a.rows * (a.k / block_elems(a.fmt));
+    const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+    switch (a.fmt) {
+        case kMXFP4: hipLaunchKernelGGL(quantize_kernel<kMXFP4>, grid, block, 0, st, a.x, a.gscale, a.codes, a.scales, a.rows, a.k); return true;
+        case kMXFP8: hipLaunchKernelGGL(quantize_kernel<kMXFP8>, grid, block, 0, st, a.x, a.gscale, a.codes, a.scales, a.rows, a.k); return true;
+        case kNVFP4: hipLaunchKernelGGL(quantize_kernel<kNVFP4>, grid, block, 0, st, a.x, a.gscale, a.codes, a.scales, a.rows, a.k); return true;
+    }
+    return false;
+}
+
+}  // namespace mxq

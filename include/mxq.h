@@ -233,6 +233,29 @@ mxq_status_t mxq_moe_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, 
                           int32_t *workspace, int64_t num_experts, int64_t m, int64_t n, int64_t k, int64_t topk,
                           void *stream);
 
+/*
+ * Block-float quantizer: bf16 values -> packed codes and block scales, the
+ * layout every other entry point reads.  The ROCm status table of the "Build
+ * from source" manual (section "Current status", row "mxfp8, mxfp4
+ * checkpoints") requantizes vendor FP8 block checkpoints to MXFP8 at load;
+ * the pages give no procedure, so the conversion is the OCP MX v1.0 one:
+ *   MX:    per 32-element block, X = 2^(floor(log2 max|v|) - emax) with emax 2
+ *          (E2M1) or 8 (E4M3), the exponent clamped to [-127, 127] (a zero
+ *          block takes -127) and stored as the E8M0 byte; codes = q(v / X).
+ *   NVFP4: per 16-element block, s = E4M3 rounding of fl32(max|v| / fl32(6 g))
+ *          for the caller's per-tensor scale g = global_scale[0] > 0;
+ *          codes = q(fl32(v / fl32(s g))), or +-0 when s is 0.
+ *   q(p):  the sign of p and |p| rounded to the nearest value of the element
+ *          format, ties to the even code, saturating at its largest value.
+ *   x       bf16 [rows][k], 16-byte aligned, finite values
+ *   codes   out [rows][k/2] (E2M1, low nibble = even k) or [rows][k] (E4M3), 16-byte aligned
+ *   scales  out [rows][k/32] (E8M0) or [rows][k/16] (E4M3)
+ *   global_scale  NVFP4: device fp32 [1], input; MX: NULL
+ *   k a positive multiple of the block size; rows * k <= 2^36
+ */
+mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale, uint8_t *codes, uint8_t *scales,
+                          int64_t rows, int64_t k, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 

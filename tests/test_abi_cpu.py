@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
-         "mxq_moe_gemm", "mxq_status_string", "mxq_abi_version"])
+         "mxq_moe_gemm", "mxq_quantize", "mxq_status_string", "mxq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,7 +74,11 @@ def mgemm(fmt=1, codes=A, scales=A, g=None, ids=A, x=A, per=0, y=A, ydt=0, ws=A,
     return mxq.lib().mxq_moe_gemm(fmt, codes, scales, g, ids, x, per, y, ydt, ws, E, m, n, k, topk, None)
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, mgemm])
+def quant(fmt=1, x=A, g=None, codes=A, scales=A, rows=4, k=64):
+    return mxq.lib().mxq_quantize(fmt, x, g, codes, scales, rows, k, None)
+
+
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, mgemm, quant])
 def test_format_errors(call):
     assert call(fmt=0) == FORMAT
     assert call(fmt=4) == FORMAT
@@ -99,6 +103,8 @@ def test_null_pointers_per_entry():
         assert block(**{arg: None}) == NULLPTR, arg
     for arg in ("ids", "x", "y", "ws"):
         assert mgemm(**{arg: None}) == NULLPTR, arg
+    for arg in ("x", "codes", "scales"):
+        assert quant(**{arg: None}) == NULLPTR, arg
 
 
 def test_shape_errors():
@@ -126,6 +132,9 @@ def test_shape_errors():
             assert mgemm(**{arg: bad}) == SHAPE, arg
     assert mgemm(k=48) == SHAPE and mgemm(fmt=3, g=A, k=16) == SHAPE  # whole 32-element blocks
     assert mgemm(ydt=2) == FORMAT
+    for bad in (0, -1):
+        assert quant(rows=bad) == SHAPE and quant(k=bad) == SHAPE
+    assert quant(k=48) == SHAPE and quant(fmt=2, k=16) == SHAPE and quant(fmt=3, g=A, k=40) == SHAPE
 
 
 def test_alignment_errors():
@@ -140,6 +149,7 @@ def test_alignment_errors():
     assert block(fmt=3, g=A, dn_g=A + 2) == ALIGN
     for arg, off in (("codes", 8), ("x", 8), ("y", 2), ("ids", 2), ("ws", 1)):
         assert mgemm(**{arg: A + off}) == ALIGN, arg
+    assert quant(x=A + 8) == ALIGN and quant(codes=A + 8) == ALIGN and quant(fmt=3, g=A + 2, k=64) == ALIGN
 
 
 def test_unsupported_sizes():
@@ -155,6 +165,7 @@ def test_unsupported_sizes():
     assert mgemm(topk=17) == UNSUPPORTED and mgemm(E=1025) == UNSUPPORTED
     assert mgemm(m=(1 << 24) // 8 + 1, topk=8) == UNSUPPORTED and mgemm(n=1 << 31) == UNSUPPORTED
     assert mgemm(k=4096) == UNSUPPORTED  # 16 padded input rows must fit 128 KiB of LDS
+    assert quant(rows=1 << 20, k=(1 << 16) + 32) == UNSUPPORTED and quant(rows=1 << 31) == UNSUPPORTED
 
 
 def _no_gpu():
@@ -167,6 +178,7 @@ def test_device_error_without_gpu():
     assert gemv() == DEVICE and moe() == DEVICE and gemm() == DEVICE and deq() == DEVICE
     assert route() == DEVICE and block() == DEVICE and mgemm() == DEVICE
     assert mgemm(m=(1 << 24) // 8, topk=8, E=1024, k=4064) == DEVICE  # largest accepted sizes
+    assert quant() == DEVICE and quant(fmt=3, g=A, k=48) == DEVICE and quant(rows=1 << 20, k=1 << 16) == DEVICE
     assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
 
