@@ -1,6 +1,7 @@
 // gemv_mfma.hpp -- dense GEMV on the matrix unit, for small batches.
 //
-// y[b][r] = sum_k W[r][k] * x[b][k] for batch <= 16, written as a 16 x 16 x 32
+// y[b][r] = sum_k W[r][k] * x[b][k] for batch <= 16 (fp32, or bf16 rounded to
+// nearest even for the small-m prefill GEMM), written as a 16 x 16 x 32
 // bf16 MFMA per k step: the A operand is 16 weight rows decoded from their
 // codes (block_operand.hpp), the B operand is x with one column per batch
 // entry (columns past the batch hold zeros), and the fp32 accumulator holds
@@ -83,7 +84,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
                                                             const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ gscale,
                                                             const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                            int64_t n, int64_t k, int batch, int64_t ntiles) {
+                                                            int64_t n, int64_t k, int batch, int64_t ntiles,
+                                                            int y_bf16) {
     using Sh = MfmaShape<FMT>;
     using Ti = MfmaTile<FMT, R, KS, NW>;
     using P = MPass<FMT, R>;
@@ -164,6 +166,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
     for (int r = 0; r < R; ++r) acc[r] = f32x4m_t{0.f, 0.f, 0.f, 0.f};
     const float gmul = (FMT == kNVFP4) ? gscale[0] : 1.0f;
 
+    auto store = [&](int64_t idx, float v) {
+        if (y_bf16) reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+        else y[idx] = v;
+    };
     auto finish = [&]() {
         const int64_t rowt = (tile0 + tc * gridDim.x) * Ti::ROWS + (int64_t)wr * R * 16;
         if constexpr (KS == 1) {
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int64_t row = rowt + r * 16 + 4 * g + i;
-                        if (row < n) y[(int64_t)lr * n + row] = acc[r][i] * gmul;
+                        if (row < n) store((int64_t)lr * n + row, acc[r][i] * gmul);
                     }
             }
         } else {
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int64_t row = rowt + r * 16 + 4 * g + i;
-                        if (row < n) y[(int64_t)lr * n + row] = v[i] * gmul;
+                        if (row < n) store((int64_t)lr * n + row, v[i] * gmul);
                     }
                 }
             }
@@ -279,10 +285,11 @@ static void launch_mfma_inst(const GemvArgs& a, int64_t per_cu, hipStream_t st) 
     const int64_t lds = a.batch * mfma_x_stride(a.k) * 2;
     if (lds <= kMfmaMaxXLds)
         hipLaunchKernelGGL((gemv_mfma_kernel<FMT, R, KS, NW, true>), dim3((unsigned)blocks), dim3(Ti::THREADS),
-                           (size_t)lds, st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles);
+                           (size_t)lds, st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles,
+                           a.y_bf16);
     else
         hipLaunchKernelGGL((gemv_mfma_kernel<FMT, R, KS, NW, false>), dim3((unsigned)blocks), dim3(Ti::THREADS), 0,
-                           st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles);
+                           st, a.codes, a.scales, a.gscale, a.x, a.y, a.n, a.k, (int)a.batch, ntiles, a.y_bf16);
 }
 
 // Compiled (rows per wave R, k split KS, waves per workgroup NW) settings.

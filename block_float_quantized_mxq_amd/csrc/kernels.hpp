@@ -17,7 +17,8 @@ struct GemvArgs {
     const uint16_t* x;
     float* y;
     int64_t n, k, batch;
-    int cus;  // compute units of the device
+    int cus;         // compute units of the device
+    int y_bf16 = 0;  // matrix-unit path only: y holds bf16 (RNE), not fp32
 };
 
 // Dense GEMV settings: lanes per row (rows_g), k split (rows_s), rows per lane

@@ -22,7 +22,9 @@ def small_case(fmt, m, n, k, seed):
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3])
-@pytest.mark.parametrize("m,n,k", [(300, 200, 256), (128, 128, 64), (1, 7, 32), (257, 129, 96)])
+@pytest.mark.parametrize("m,n,k", [(300, 200, 256), (128, 128, 64), (1, 7, 32), (257, 129, 96), (2, 300, 5120),
+                                   (5, 77, 256), (9, 129, 96), (16, 1000, 512), (17, 200, 256), (32, 64, 128),
+                                   (33, 96, 64)])
 def test_gemm_all_outputs(fmt, m, n, k):
     c = small_case(fmt, m, n, k, m + n + k + fmt)
     say("gemm", fmt, m, n, k)
@@ -33,8 +35,10 @@ def test_gemm_all_outputs(fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt", [1, 3])
-def test_bf16_output_is_rne_of_fp32(fmt):
-    c = small_case(fmt, 260, 300, 512, 11)
+@pytest.mark.parametrize("m", [260, 3, 16, 29])
+def test_bf16_output_is_rne_of_fp32(fmt, m):
+    """Both paths: 256 x 256 tiles (m > 32) and the matrix-unit GEMV (m <= 32, 16 rows a launch)."""
+    c = small_case(fmt, m, 300, 512, 11)
     args = (fmt, dev_u8(c["codes"]), dev_u8(c["scales"]), dev_bf16(c["x"]), dev_f32(c["g"]))
     say("gemm bf16 epilogue", fmt)
     y32 = mxq.gemm(*args, out_dtype=torch.float32)
