@@ -150,22 +150,25 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         __syncthreads();  // the previous block's LDS reads are done
         if (tid < batch) xrow_of[tid] = gperm[c0 + t0 + tid] / xdiv;
         __syncthreads();
-        // gather the input rows of this block's pairs: rows b0 .. b0 + U - 1
-        // per round, 16-byte piece c of each (U loads per thread in flight)
-        constexpr int U = 4;
-        const int pieces = (int)(k / 8);
-        for (int b0 = 0; b0 < batch; b0 += U) {
-            for (int c = tid; c < pieces; c += NW * 64) {
-                u32x4g_t v[U];
+        // gather the input rows of this block's pairs: piece i of the block is
+        // row i / pieces, 16-byte column i % pieces; U pieces per thread in
+        // flight (all of a 16 x 2048 block in one round)
+        constexpr int U = 8, NT = NW * 64;
+        const int pieces = (int)(k / 8), total = batch * pieces;
+        for (int i0 = tid; i0 < total; i0 += U * NT) {
+            u32x4g_t v[U];
+            int bi[U], ci[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int b = b0 + u < batch ? b0 + u : b0;
-                    v[u] = *reinterpret_cast<const u32x4g_t*>(x + xrow_of[b] * k + (int64_t)c * 8);
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (b0 + u < batch) reinterpret_cast<u32x4g_t*>(xlds)[(int64_t)(b0 + u) * (xstride / 8) + c] = v[u];
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * NT < total ? i0 + u * NT : i0;
+                bi[u] = i / pieces;
+                ci[u] = i - bi[u] * pieces;
+                v[u] = *reinterpret_cast<const u32x4g_t*>(x + xrow_of[bi[u]] * k + (int64_t)ci[u] * 8);
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * NT < total)
+                    reinterpret_cast<u32x4g_t*>(xlds)[(int64_t)bi[u] * (xstride / 8) + ci[u]] = v[u];
         }
         __syncthreads();
 
