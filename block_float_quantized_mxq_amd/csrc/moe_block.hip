@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* _
         lv[e] = v;
         mx = v > mx ? v : mx;
     }
-    for (int e = E + tid; e < ((E + 3) & ~3); e += kRouteThreads) lv[e] = -__builtin_huge_valf();  // pad to 4
+    for (int e = E + tid; e < ((E + 15) & ~15); e += kRouteThreads) lv[e] = -__builtin_huge_valf();  // pad to 16
     mx = wave_max(mx);
     if ((tid & 63) == 0) part[wave] = mx;
     __syncthreads();
@@ -110,13 +110,21 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* _
 
     for (int e = tid; e < E; e += kRouteThreads) {
         const float v = lv[e];
+        // 16 logits per step: four independent LDS reads in flight (the
+        // padding never counts: -inf beats nothing, and its index is past e)
         int rank = 0;
-        for (int j = 0; j < E; j += 4) {
-            const float4 o = *reinterpret_cast<const float4*>(lv + j);
-            rank += (o.x > v || (o.x == v && j < e)) ? 1 : 0;
-            rank += (o.y > v || (o.y == v && j + 1 < e)) ? 1 : 0;
-            rank += (o.z > v || (o.z == v && j + 2 < e)) ? 1 : 0;
-            rank += (o.w > v || (o.w == v && j + 3 < e)) ? 1 : 0;
+        for (int j0 = 0; j0 < E; j0 += 16) {
+            float4 o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const float4*>(lv + j0 + 4 * q);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = j0 + 4 * q;
+                rank += (o[q].x > v || (o[q].x == v && j < e)) ? 1 : 0;
+                rank += (o[q].y > v || (o[q].y == v && j + 1 < e)) ? 1 : 0;
+                rank += (o[q].z > v || (o[q].z == v && j + 2 < e)) ? 1 : 0;
+                rank += (o[q].w > v || (o[q].w == v && j + 3 < e)) ? 1 : 0;
+            }
         }
         if (rank < topk) {
             ids[t * topk + rank] = e;
