@@ -259,7 +259,7 @@ mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale,
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3 (2 plus mxq_moe_gemm and mxq_quantize). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 2
+    assert lib.mxq_abi_version() == 3
 
 
 def test_status_strings():
