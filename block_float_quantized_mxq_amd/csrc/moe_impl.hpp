@@ -34,11 +34,16 @@ constexpr int64_t kMoeMaxXLds = 64 * 1024;
 #endif
 constexpr int kMoeAhead = MXQ_MOE_AHEAD;
 
-// Pairs per round: at most one per token when a token's experts are distinct,
-// so rounds of min(8, tokens) pairs (rounded up to 1, 2, 4, 8); repeated ids
-// only add rounds.  LDS holds one round's activations.
+// Pairs per round: 1 at one token, 2 up to four tokens, 4 beyond.  A token's
+// experts are distinct, so an expert gets at most `tokens` pairs, and with 128
+// experts rarely more than one or two; experts with more pairs than the cap
+// take extra rounds (their rows come from L2 the second time).  A smaller cap
+// keeps the registers of the smaller batch (MI355X, 30B-A3B bank: 4 tokens
+// gate/up 15.9 -> 13.7 us and down 12.3 -> 9.6 us with 2 instead of 4; 8
+// tokens 36.7 -> 29.5 us and 22.9 -> 18.7 us with 4 instead of 8).  LDS holds
+// one round's activations.
 static int moe_round_cap(int64_t tokens) {
-    return tokens <= 1 ? 1 : (tokens <= 2 ? 2 : (tokens <= 4 ? 4 : 8));
+    return tokens <= 1 ? 1 : (tokens <= 4 ? 2 : 4);
 }
 
 // Takes the next routing position from the two 64-bit masks (positions 0..63
@@ -179,7 +184,7 @@ static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
 // MI355X measurements: rows of >= 64 chunks take 16 lanes and 2 rows per
-// lane up to two tokens and 8 lanes with one row per lane beyond; shorter
+// lane up to four tokens and 8 lanes with one row per lane beyond; shorter
 // rows take 8 lanes up to two tokens and 4 lanes beyond (more rows per
 // workgroup for the same activations).  MXQ_MOE_ROWS="g,s,r" overrides the
 // choice (used only to compare variants when tuning).
@@ -190,7 +195,7 @@ static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     if (nchunks < 64) {
         r = 1;
         g = (a.tokens <= 2 && nchunks >= 8) ? 8 : 4;
-    } else if (a.tokens >= 3) {
+    } else if (a.tokens >= 5) {
         g = 8;
         r = 1;
     }
