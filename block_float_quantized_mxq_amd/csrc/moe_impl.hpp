@@ -34,16 +34,16 @@ constexpr int64_t kMoeMaxXLds = 64 * 1024;
 #endif
 constexpr int kMoeAhead = MXQ_MOE_AHEAD;
 
-// Pairs per round: 1 at one token, 2 up to four tokens, 4 beyond.  A token's
-// experts are distinct, so an expert gets at most `tokens` pairs, and with 128
-// experts rarely more than one or two; experts with more pairs than the cap
-// take extra rounds (their rows come from L2 the second time).  A smaller cap
-// keeps the registers of the smaller batch (MI355X, 30B-A3B bank: 4 tokens
-// gate/up 15.9 -> 13.7 us and down 12.3 -> 9.6 us with 2 instead of 4; 8
-// tokens 36.7 -> 29.5 us and 22.9 -> 18.7 us with 4 instead of 8).  LDS holds
-// one round's activations.
+// Pairs per round: 1 at one token, else 2.  A token's experts are distinct, so
+// an expert gets at most `tokens` pairs, and with 128 experts rarely more than
+// one or two; an expert with more pairs than the cap takes extra rounds (its
+// rows come from L2 the second time).  The small cap keeps the registers of a
+// two-vector loop (MI355X, 30B-A3B bank, against rounds of min(8, tokens)
+// rounded up to a power of two: 4 tokens gate/up 15.9 -> 13.7 us, down 12.3 ->
+// 9.5 us; 8 tokens 36.7 -> 23.4 us, 22.9 -> 16.1 us; rounds of one pair were
+// within 5% at 2 and 4 tokens).  LDS holds one round's activations.
 static int moe_round_cap(int64_t tokens) {
-    return tokens <= 1 ? 1 : (tokens <= 4 ? 2 : 4);
+    return tokens <= 1 ? 1 : 2;
 }
 
 // Takes the next routing position from the two 64-bit masks (positions 0..63
@@ -174,12 +174,8 @@ static void launch_moe_rc(const MoeArgs& a, hipStream_t st) {
 
 template <int FMT, int CB, int G, int S, int R>
 static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
-    switch (moe_round_cap(a.tokens)) {
-        case 1: launch_moe_rc<FMT, CB, G, S, R, 1>(a, st); break;
-        case 2: launch_moe_rc<FMT, CB, G, S, R, 2>(a, st); break;
-        case 4: launch_moe_rc<FMT, CB, G, S, R, 4>(a, st); break;
-        default: launch_moe_rc<FMT, CB, G, S, R, 8>(a, st); break;
-    }
+    if (moe_round_cap(a.tokens) == 1) launch_moe_rc<FMT, CB, G, S, R, 1>(a, st);
+    else launch_moe_rc<FMT, CB, G, S, R, 2>(a, st);
 }
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
