@@ -237,14 +237,24 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t* __res
     eng.template run<1>(cur, ring, xs, ys, 1.0f, red, xlds, smul, topk);
 }
 
-template <int FMT, int CB, int G, int S>
+template <int FMT, int CB, int G, int S, int R>
 static void launch_down_inst(const MoeBlockArgs& a, hipStream_t st) {
-    using T = RowTile<G, S, 2>;
+    using T = RowTile<G, S, R>;
     const int64_t tiles = (a.hidden + T::ROWS - 1) / T::ROWS;
     const size_t lds = (size_t)S * a.dff * 2;
-    hipLaunchKernelGGL((moe_down_kernel<FMT, CB, G, S, 2>), dim3((unsigned)tiles, (unsigned)a.tokens), dim3(kThreads),
+    hipLaunchKernelGGL((moe_down_kernel<FMT, CB, G, S, R>), dim3((unsigned)tiles, (unsigned)a.tokens), dim3(kThreads),
                        lds, st, a.dn_codes, a.dn_scales, a.dn_gscale, a.ids, a.weights, a.h, a.y, a.experts, a.hidden,
                        a.dff, (int)a.topk);
+}
+
+// Rows per lane: a workgroup builds its token's activations once for all its
+// rows, so from two tokens 4 rows per lane (half the workgroups, half the
+// rebuilt activations) beat 2 (MI355X, 30B-A3B block: 4 tokens 33.0 -> 30.0 us,
+// 8 tokens 49.6 -> 45.0 us; one token 18.0 vs 18.6 us, so 2 there).
+template <int FMT, int CB, int G, int S>
+static void launch_down_gs(const MoeBlockArgs& a, hipStream_t st) {
+    if (a.tokens >= 2) launch_down_inst<FMT, CB, G, S, 4>(a, st);
+    else launch_down_inst<FMT, CB, G, S, 2>(a, st);
 }
 
 // Slots rounded up to a power of two; 8 lanes per row while a slot's row has
@@ -254,11 +264,11 @@ static bool launch_down_cb(const MoeBlockArgs& a, hipStream_t st) {
     const int64_t chunks = code_bytes_per_row(FMT, a.dff) / CB;
     const bool narrow = chunks <= 32;
     switch (a.topk <= 1 ? 1 : a.topk <= 2 ? 2 : a.topk <= 4 ? 4 : a.topk <= 8 ? 8 : 16) {
-        case 1: narrow ? launch_down_inst<FMT, CB, 8, 1>(a, st) : launch_down_inst<FMT, CB, 16, 1>(a, st); return true;
-        case 2: narrow ? launch_down_inst<FMT, CB, 8, 2>(a, st) : launch_down_inst<FMT, CB, 16, 2>(a, st); return true;
-        case 4: narrow ? launch_down_inst<FMT, CB, 8, 4>(a, st) : launch_down_inst<FMT, CB, 16, 4>(a, st); return true;
-        case 8: narrow ? launch_down_inst<FMT, CB, 8, 8>(a, st) : launch_down_inst<FMT, CB, 16, 8>(a, st); return true;
-        default: narrow ? launch_down_inst<FMT, CB, 8, 16>(a, st) : launch_down_inst<FMT, CB, 16, 16>(a, st); return true;
+        case 1: narrow ? launch_down_gs<FMT, CB, 8, 1>(a, st) : launch_down_gs<FMT, CB, 16, 1>(a, st); return true;
+        case 2: narrow ? launch_down_gs<FMT, CB, 8, 2>(a, st) : launch_down_gs<FMT, CB, 16, 2>(a, st); return true;
+        case 4: narrow ? launch_down_gs<FMT, CB, 8, 4>(a, st) : launch_down_gs<FMT, CB, 16, 4>(a, st); return true;
+        case 8: narrow ? launch_down_gs<FMT, CB, 8, 8>(a, st) : launch_down_gs<FMT, CB, 16, 8>(a, st); return true;
+        default: narrow ? launch_down_gs<FMT, CB, 8, 16>(a, st) : launch_down_gs<FMT, CB, 16, 16>(a, st); return true;
     }
 }
 
