@@ -33,10 +33,6 @@ __device__ __forceinline__ float quant_mag(float a, int mbits, int emin, float m
     return v > maxv ? maxv : v;
 }
 
-__device__ __forceinline__ uint32_t e2m1_code(float r) {  // r in {0, .5, 1, 1.5, 2, 3, 4, 6}
-    return r < 2.0f ? (uint32_t)(r * 2.0f) : (r < 4.0f ? (r == 3.0f ? 5u : 4u) : (r == 6.0f ? 7u : 6u));
-}
-
 __device__ __forceinline__ uint32_t e4m3_code(float r) {  // r a representable E4M3 magnitude
     if (r < 0.015625f) return (uint32_t)(r * 512.0f);     // subnormal: multiples of 2^-9
     const int e = __builtin_amdgcn_frexp_expf(r) - 1;
@@ -92,20 +88,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     }
 
     uint32_t out[FMT == kMXFP8 ? BS / 4 : BS / 8] = {};
+    if constexpr (FMT == kMXFP8) {
+        // E4M3 codes rounded in software: the hardware conversion differs from
+        // the definition on some inputs (measured on MI355X)
 #pragma unroll
-    for (int j = 0; j < BS; ++j) {
-        const uint32_t bits = (j & 1) ? (w[j / 2] >> 16) : (w[j / 2] & 0xFFFFu);
-        const float v = __builtin_bit_cast(float, bits << 16);
-        float p;
-        if constexpr (FMT == kNVFP4) p = zero ? 0.0f : v / den;
-        else p = v * mul;
-        const uint32_t neg = bits >> 15;
-        if constexpr (FMT == kMXFP8) {
-            const uint32_t c = e4m3_code(quant_mag(__builtin_fabsf(p), 3, -6, 448.0f)) | (neg << 7);
+        for (int j = 0; j < BS; ++j) {
+            const uint32_t bits = (j & 1) ? (w[j / 2] >> 16) : (w[j / 2] & 0xFFFFu);
+            const float p = __builtin_bit_cast(float, bits << 16) * mul;
+            const uint32_t c = e4m3_code(quant_mag(__builtin_fabsf(p), 3, -6, 448.0f)) | ((bits >> 15) << 7);
             out[j / 4] |= c << (8 * (j % 4));
-        } else {
-            const uint32_t c = e2m1_code(quant_mag(__builtin_fabsf(p), 1, 0, 6.0f)) | (neg << 3);
-            out[j / 8] |= c << (4 * (j % 8));
+        }
+    } else {
+        // E2M1 codes by the hardware conversion with a unit scale operand: it
+        // rounds to nearest with ties to even, saturates and keeps the sign,
+        // as the definition does (checked bit for bit against the oracle on
+        // ties, saturating quotients and signed zeros)
+#pragma unroll
+        for (int j = 0; j < BS; j += 2) {
+            const float v0 = bf16_lo_to_f32(w[j / 2]), v1 = bf16_hi_to_f32(w[j / 2]);
+            float p0, p1;
+            if constexpr (FMT == kNVFP4) {
+                p0 = zero ? __builtin_copysignf(0.0f, v0) : v0 / den;
+                p1 = zero ? __builtin_copysignf(0.0f, v1) : v1 / den;
+            } else {
+                p0 = v0 * mul;
+                p1 = v1 * mul;
+            }
+            const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p0, p1, 1.0f, 0);
+            out[j / 8] |= (c & 0xFFu) << (4 * (j % 8));
         }
     }
     if constexpr (FMT == kMXFP8) {
