@@ -89,14 +89,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 
     uint32_t out[FMT == kMXFP8 ? BS / 4 : BS / 8] = {};
     if constexpr (FMT == kMXFP8) {
-        // E4M3 codes rounded in software: the hardware conversion differs from
-        // the definition on some inputs (measured on MI355X)
+        // E4M3 codes by the hardware conversion with a unit scale operand, the
+        // quotients first clamped to +-448: the conversion does not saturate
+        // the way the definition does (quotients reach 512), the rest matches
+        // it bit for bit
+        typedef short s16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int j = 0; j < BS; ++j) {
-            const uint32_t bits = (j & 1) ? (w[j / 2] >> 16) : (w[j / 2] & 0xFFFFu);
-            const float p = __builtin_bit_cast(float, bits << 16) * mul;
-            const uint32_t c = e4m3_code(quant_mag(__builtin_fabsf(p), 3, -6, 448.0f)) | ((bits >> 15) << 7);
-            out[j / 4] |= c << (8 * (j % 4));
+        for (int j = 0; j < BS; j += 2) {
+            const float p0 = __builtin_fminf(__builtin_fmaxf(bf16_lo_to_f32(w[j / 2]) * mul, -448.0f), 448.0f);
+            const float p1 = __builtin_fminf(__builtin_fmaxf(bf16_hi_to_f32(w[j / 2]) * mul, -448.0f), 448.0f);
+            const s16x2_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2_t{0, 0}, p0, p1, 1.0f, false);
+            out[j / 4] |= ((uint32_t)(uint16_t)hw[0]) << (8 * (j % 4));
         }
     } else {
         // E2M1 codes by the hardware conversion with a unit scale operand: it
