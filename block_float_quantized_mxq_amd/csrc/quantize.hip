@@ -106,18 +106,45 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         // rounds to nearest with ties to even, saturates and keeps the sign,
         // as the definition does (checked bit for bit against the oracle on
         // ties, saturating quotients and signed zeros)
+        float p[BS];
+        if constexpr (FMT == kNVFP4) {
+            // p = RN(v / den).  One correctly rounded reciprocal y = RN(1/den)
+            // per block, then per element q0 = RN(v y) and the residual step
+            // RN(q0 + (v - q0 den) y) (Markstein's correction, both by fma):
+            // that is the correctly rounded quotient whenever every
+            // intermediate stays a normal number, which the exponent bounds
+            // below guarantee (verified exhaustively for every fp32 den and
+            // bf16 v mantissa).  Other operands, zeros among them, take the
+            // division itself.
+            const bool blk_fast = !zero && den >= 0x1p-40f && den <= 0x1p40f;
+            const float y = blk_fast ? 1.0f / den : 1.0f;
+            bool slow = false;
+#pragma unroll
+            for (int j = 0; j < BS; ++j) {
+                const float v = (j & 1) ? bf16_hi_to_f32(w[j / 2]) : bf16_lo_to_f32(w[j / 2]);
+                const float a = __builtin_fabsf(v);
+                const bool fast = blk_fast && a >= 0x1p-30f && a <= 0x1p80f;
+                const float q0 = __fmul_rn(v, y);
+                const float rsd = __builtin_fmaf(-q0, den, v);
+                p[j] = __builtin_fmaf(rsd, y, q0);
+                slow |= !fast;
+            }
+            if (slow) {
+#pragma unroll
+                for (int j = 0; j < BS; ++j) {
+                    const float v = (j & 1) ? bf16_hi_to_f32(w[j / 2]) : bf16_lo_to_f32(w[j / 2]);
+                    const float a = __builtin_fabsf(v);
+                    const bool fast = blk_fast && a >= 0x1p-30f && a <= 0x1p80f;
+                    if (!fast) p[j] = zero ? __builtin_copysignf(0.0f, v) : v / den;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < BS; ++j) p[j] = ((j & 1) ? bf16_hi_to_f32(w[j / 2]) : bf16_lo_to_f32(w[j / 2])) * mul;
+        }
 #pragma unroll
         for (int j = 0; j < BS; j += 2) {
-            const float v0 = bf16_lo_to_f32(w[j / 2]), v1 = bf16_hi_to_f32(w[j / 2]);
-            float p0, p1;
-            if constexpr (FMT == kNVFP4) {
-                p0 = zero ? __builtin_copysignf(0.0f, v0) : v0 / den;
-                p1 = zero ? __builtin_copysignf(0.0f, v1) : v1 / den;
-            } else {
-                p0 = v0 * mul;
-                p1 = v1 * mul;
-            }
-            const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p0, p1, 1.0f, 0);
+            const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[j], p[j + 1], 1.0f, 0);
             out[j / 8] |= (c & 0xFFu) << (4 * (j % 8));
         }
     }

@@ -56,6 +56,19 @@ def test_special_blocks_match_oracle(fmt):
         check(fmt, x, g, f"quantize special {FMT_NAMES[fmt]} g={g}")
 
 
+@pytest.mark.parametrize("g", [2.0 ** -60, 1e-30, 1.0, 2.0 ** 60, 3.0e5])
+def test_nvfp4_quotients_over_the_whole_exponent_range(g):
+    """NVFP4 element quotients v / fl32(s g) with v over bf16's whole exponent
+    range and global scales that put fl32(s g) far from 1: every path of the
+    quotient (one reciprocal per block plus a residual step, and the plain
+    division for operands and scales far from 1) against the oracle's
+    division, bit for bit."""
+    rng = np.random.default_rng(int(np.log2(g) + 200) if g > 0 else 1)
+    x = bf16_spread(rng, 96, 512, -125, 126)
+    x[::7] = bf16_spread(rng, 14, 512, -3, 3)  # every 7th row: one narrow range, quotients near the grid
+    check(3, x, float(np.float32(g)), f"quantize nvfp4 wide exponents g={g}")
+
+
 @pytest.mark.parametrize("fmt", [1, 2])
 def test_roundtrip_through_device_decode(fmt):
     """Weights whose blocks peak at the format's top binade: GPU dequant -> bf16 ->
