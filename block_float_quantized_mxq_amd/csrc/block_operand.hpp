@@ -6,9 +6,10 @@
 // The MFMA sums over k, so the k order inside a slice may be permuted as long
 // as both operands use the same permutation; giving every lane one whole
 // block per slice makes its codes one 16-byte (32 for E4M3) load with one
-// scale byte.  The decode is exact: every E2M1 / E4M3 value times an E8M0
-// scale is a bf16 wherever it is a normal number, and an E2M1 value times an
-// E4M3 scale has at most 6 significant bits.
+// scale byte.  The decode is exact: every E2M1 value times an E8M0 scale is a
+// bf16 (or overflows as it does in fp32), so is every E4M3 value at E8M0 bytes
+// of kMx8Lift and above (lower bytes: the split below), and an E2M1 value
+// times an E4M3 scale has at most 6 significant bits.
 #pragma once
 
 #include "mxq_device.hpp"
@@ -93,6 +94,29 @@ __device__ __forceinline__ bf16x8_t decode_step(const WFrag<FMT>& f) {
         d[3] = scaled_fp4x2_to_bf16x2<3>(f.w[S], s);
     }
     return __builtin_bit_cast(bf16x8_t, u32x4g_t{d[0], d[1], d[2], d[3]});
+}
+
+// MXFP8 fragments whose E8M0 byte is below kMx8Lift (mxq_device.hpp) are not
+// exact in bf16.  A wave holding one splits each fragment in two operands:
+// the plain part (lifted fragments' codes zeroed) and the lifted part (the
+// other fragments' codes zeroed, lifted fragments decoded with byte
+// u + kMx8Lift).  The plain part goes into the accumulator as usual; the
+// lifted part into a separate sum that is multiplied by 2^-kMx8Lift in fp32.
+template <int FMT>
+__device__ __forceinline__ bool frag_lifted(const WFrag<FMT>& f) {
+    return mx_lifted<FMT>(f.s);
+}
+
+template <int FMT, int S, bool LIFTED>
+__device__ __forceinline__ bf16x8_t decode_step_part(const WFrag<FMT>& f) {
+    static_assert(FMT == kMXFP8, "only MXFP8 fragments are lifted");
+    const bool lo = frag_lifted<FMT>(f);
+    const bool keep = LIFTED ? lo : !lo;
+    WFrag<FMT> g;
+#pragma unroll
+    for (int d = 0; d < WFrag<FMT>::DW; ++d) g.w[d] = keep ? f.w[d] : 0u;
+    g.s = LIFTED ? (lo ? f.s + kMx8Lift : 127u) : f.s;
+    return decode_step<FMT, S>(g);
 }
 
 }  // namespace mxq

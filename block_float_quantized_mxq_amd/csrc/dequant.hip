@@ -1,13 +1,19 @@
-// dequant.hip -- decode-only kernel: block-float weights to fp32, using the
-// same register decode as the GEMV, MoE and GEMM kernels, so that the decode
-// can be checked bit for bit.
+// dequant.hip -- decode-only kernel: block-float weights to fp32 through the
+// very decode the GEMV, MoE and GEMM kernels run, so that the decode can be
+// checked bit for bit against the format definitions.
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
 namespace mxq {
 
-// One thread per code chunk: w[r][j] = fl32(q * 2^(u-127)) (MX) or
-// fl32((q * s) * g) (NVFP4), using the same register decode as the GEMV.
+// One thread per code chunk.  MX formats: the codes go through the scaled
+// conversion with the block's E8M0 byte in its scale operand (bf16 out), as
+// in every product kernel; MXFP8 blocks with a byte below kMx8Lift are
+// decoded with byte u + kMx8Lift and multiplied by 2^-kMx8Lift in fp32, as
+// the product kernels scale their partial sums.  NVFP4: unit-scale decode,
+// times the E4M3 block scale in fp32 (exact: q * s has at most 6 significant
+// bits), times the per-tensor scale g.  The result is w = fl32(q * 2^(u-127))
+// or fl32((q * s) * g) for every code and every scale byte.
 template <int FMT, int CB>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
@@ -22,18 +28,27 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     const uint8_t* srow = scales + r * (k / CS::BS);
     uint32_t cw[CS::DW];
     load_code_chunk<CB>(codes + r * rowbytes + c * CB, cw);
+    uint32_t sb[CS::NSG];
+    load_scale_bytes<FMT, CB>(srow, c, sb);
     uint32_t wp[CS::NP];
-    decode_dwords<FMT, CS::DW>(cw, wp);
+    float mul[CS::NSG];
+    if constexpr (FMT == kNVFP4) {
+        decode_dwords<FMT, CS::DW>(cw, wp);
+#pragma unroll
+        for (int q = 0; q < CS::NSG; ++q) mul[q] = e4m3_to_f32(sb[q]);
+    } else {
+        const uint32_t u = sb[0];
+        const bool lo = mx_lifted<FMT>(u);
+        decode_dwords_scaled<FMT, CS::DW>(cw, e8m0_exponent(lo ? u + kMx8Lift : u), wp);
+        mul[0] = lo ? kMx8Unlift : 1.0f;
+    }
     float* out = w + r * k + c * CS::KPC;
     const float g = (FMT == kNVFP4) ? gscale[0] : 1.0f;
 #pragma unroll
     for (int t = 0; t < CS::NP; ++t) {
-        const int64_t e = c * CS::KPC + 2 * t;  // element index within the row
-        float s;
-        if constexpr (FMT == kNVFP4) s = e4m3_to_f32(srow[e / 16]);
-        else s = e8m0_to_f32(srow[e / 32]);
-        float lo = bf16_lo_to_f32(wp[t]) * s;
-        float hi = bf16_hi_to_f32(wp[t]) * s;
+        const float m = mul[t / CS::PPS];
+        float lo = bf16_lo_to_f32(wp[t]) * m;
+        float hi = bf16_hi_to_f32(wp[t]) * m;
         if constexpr (FMT == kNVFP4) {
             lo *= g;
             hi *= g;

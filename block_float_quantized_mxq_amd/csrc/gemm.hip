@@ -19,9 +19,10 @@
 //    for A and B (the sum does not depend on it): in k step s the lanes of
 //    half g take k = g*32 + s*8 .. +7, so each lane's codes for the whole
 //    slice are one 32-element block, one 16-byte load (32 for E4M3) with one
-//    scale byte.  E8M0 scales go into the conversion (exact wherever the
-//    decoded weight is a normal bf16); NVFP4's E4M3 scales multiply in fp32
-//    (q * s has at most 6 significant bits, so its bf16 is exact).
+//    scale byte.  E8M0 scales go into the conversion (exact at every byte;
+//    MXFP8 fragments with a byte below kMx8Lift are split, block_operand.hpp);
+//    NVFP4's E4M3 scales multiply in fp32 (q * s has at most 6 significant
+//    bits, so its bf16 is exact).
 //  * Slices are pipelined: while slice s is multiplied, slice s+1's X waits in
 //    registers (stored to the other LDS buffer after the MFMAs) and its W
 //    codes are already in registers; slice s+2 is requested after them.  One
@@ -157,14 +158,45 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[i], bo[j], acc[i][j], 0, 0, 0);
         };
-        operands(std::integral_constant<int, 0>{}, a[0], b[0]);
-        operands(std::integral_constant<int, 1>{}, a[1], b[1]);
-        mfmas(a[0], b[0]);
-        operands(std::integral_constant<int, 2>{}, a[0], b[0]);
-        mfmas(a[1], b[1]);
-        operands(std::integral_constant<int, 3>{}, a[1], b[1]);
-        mfmas(a[0], b[0]);
-        mfmas(a[1], b[1]);
+        // MXFP8 slices holding a fragment with an E8M0 byte below kMx8Lift run
+        // the split form (block_operand.hpp); the branch is uniform over the wave
+        bool split = false;
+        if constexpr (FMT == kMXFP8) split = __ballot(frag_lifted<FMT>(wf[0]) || frag_lifted<FMT>(wf[1])) != 0;
+        if (!split) {
+            operands(std::integral_constant<int, 0>{}, a[0], b[0]);
+            operands(std::integral_constant<int, 1>{}, a[1], b[1]);
+            mfmas(a[0], b[0]);
+            operands(std::integral_constant<int, 2>{}, a[0], b[0]);
+            mfmas(a[1], b[1]);
+            operands(std::integral_constant<int, 3>{}, a[1], b[1]);
+            mfmas(a[0], b[0]);
+            mfmas(a[1], b[1]);
+        } else if constexpr (FMT == kMXFP8) {
+            // plain part into the accumulators
+            static_for<0, 4>([&](auto step) {
+                constexpr int S = decltype(step)::value;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) b[0][j] = decode_step_part<FMT, S, false>(wf[j]);
+                mfmas(a[0], b[0]);
+            });
+            // lifted part: one output tile at a time, scaled back in fp32
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x16_t t;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) t[e] = 0.0f;
+                    static_for<0, 4>([&](auto step) {
+                        constexpr int S = decltype(step)::value;
+                        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
+                        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, decode_step_part<FMT, S, true>(wf[j]), t, 0, 0, 0);
+                    });
+                    acc[i][j] += t * kMx8Unlift;
+                }
+        }
     };
 
     // Slice s uses LDS buffer s & 1 and W set s & 1 (wa even, wb odd).  Loads

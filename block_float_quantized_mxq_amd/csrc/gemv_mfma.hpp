@@ -208,6 +208,17 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
     };
 
     auto compute = [&](const P& p) {
+        // MXFP8 passes holding a block with an E8M0 byte below kMx8Lift run the
+        // split form (block_operand.hpp); the branch is uniform over the wave
+        bool lifted = false;
+        if constexpr (FMT == kMXFP8) {
+            bool lo = false;
+#pragma unroll
+            for (int u = 0; u < Sh::U; ++u)
+#pragma unroll
+                for (int r = 0; r < R; ++r) lo = lo || (((p.valid >> u) & 1u) && frag_lifted<FMT>(p.w[r][u]));
+            lifted = __ballot(lo) != 0;
+        }
 #pragma unroll
         for (int u = 0; u < Sh::U; ++u) {
             const bool ok = (p.valid >> u) & 1u;
@@ -238,6 +249,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(const uint8_t* __res
 #pragma unroll
                 for (int d = 0; d < WFrag<FMT>::DW; ++d) f.w[d] = ok ? f.w[d] : 0u;
                 f.s = ok ? f.s : (FMT == kNVFP4 ? 0x3838u : 127u);
+                if constexpr (FMT == kMXFP8) {
+                    if (lifted) {
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, false>(f), b[0], acc[r], 0, 0, 0);
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, false>(f), b[1], acc[r], 0, 0, 0);
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, false>(f), b[2], acc[r], 0, 0, 0);
+                        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, false>(f), b[3], acc[r], 0, 0, 0);
+                        f32x4m_t t = {0.f, 0.f, 0.f, 0.f};
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, true>(f), b[0], t, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, true>(f), b[1], t, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, true>(f), b[2], t, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, true>(f), b[3], t, 0, 0, 0);
+                        acc[r] += t * kMx8Unlift;
+                        continue;
+                    }
+                }
                 acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(f), b[0], acc[r], 0, 0, 0);
                 acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(f), b[1], acc[r], 0, 0, 0);
                 acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(f), b[2], acc[r], 0, 0, 0);

@@ -143,6 +143,15 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         w[j].s = ok ? w[j].s : (FMT == kNVFP4 ? 0x3838u : 127u);
     }
     const int64_t xstride = mfma_x_stride(k);
+    // MXFP8 weights with an E8M0 byte below kMx8Lift anywhere in the wave:
+    // every block runs the split form (block_operand.hpp); uniform over the wave
+    bool lifted = false;
+    if constexpr (FMT == kMXFP8) {
+        bool lo = false;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) lo = lo || frag_lifted<FMT>(w[j]);
+        lifted = __ballot(lo) != 0;
+    }
 
     for (int64_t t0 = 0; t0 < cnt; t0 += kPairsPerBlock) {
         const int batch = (int)(cnt - t0 < kPairsPerBlock ? cnt - t0 : kPairsPerBlock);
@@ -193,10 +202,27 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
             // (which would hold every block's operands in registers at once)
             if (j + 1 < MB) read_x(j + 1, vb[(j + 1) & 1]);
             const u32x4g_t(&v)[4] = vb[j & 1];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 3>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
+            bool split = false;
+            if constexpr (FMT == kMXFP8) split = lifted;
+            if (split) {
+                if constexpr (FMT == kMXFP8) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
+                    f32x4m_t t = {0.f, 0.f, 0.f, 0.f};
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), t, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), t, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), t, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), t, 0, 0, 0);
+                    acc += t * kMx8Unlift;
+                }
+            } else {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 3>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
+            }
             asm volatile("" ::: "memory");
         }
 

@@ -62,8 +62,9 @@ __device__ __forceinline__ void decode_dwords(const uint32_t (&c)[DW], uint32_t 
 // Same with an E8M0 block scale applied by the conversion: `sexp` is an fp32
 // whose exponent field is the E8M0 byte (the conversion uses only the
 // exponent of its scale operand, so byte 0 means 2^-127 and byte 255 gives
-// NaN, as the format defines).  Each result is bf16(q * 2^(u-127)), exact
-// wherever that is a normal bf16.
+// NaN, as the format defines).  Each result is q * 2^(u-127) rounded to bf16:
+// exact for every E2M1 code at every byte, and for every E4M3 code at bytes
+// of kMx8Lift and above (see below).
 template <int FMT, int DW>
 __device__ __forceinline__ void decode_dwords_scaled(const uint32_t (&c)[DW], float sexp,
                                                      uint32_t (&p)[(FMT == kMXFP8) ? 2 * DW : 4 * DW]) {
@@ -83,6 +84,21 @@ __device__ __forceinline__ void decode_dwords_scaled(const uint32_t (&c)[DW], fl
 
 // E8M0 byte as the exponent field of an fp32 (the scale operand above).
 __device__ __forceinline__ float e8m0_exponent(uint32_t u) { return __builtin_bit_cast(float, (u & 0xFFu) << 23); }
+
+// Exactness of the scaled conversion, measured on gfx950 over every code and
+// every E8M0 byte: the result is q * 2^(u-127) rounded to nearest even in bf16,
+// with bf16 subnormals, overflow to infinity and NaN for byte 255 (whatever the
+// code).  An E2M1 value has at most two significant bits and is at least 2^-1,
+// so every MXFP4 result is a bf16 (or overflows in fp32 just the same).  An
+// E4M3 value keeps four significant bits down to 2^-9, so q * 2^(u-127) needs
+// bits down to 2^(u-136), finer than bf16's smallest subnormal step 2^-133
+// when u < 3.  MXFP8 blocks with such a byte are "lifted": decoded with byte
+// u + kMx8Lift (exact) and their fp32 contribution multiplied by
+// 2^-kMx8Lift, which restores q * 2^(u-127) exactly in fp32.
+constexpr uint32_t kMx8Lift = 3;
+constexpr float kMx8Unlift = 0.125f;  // 2^-kMx8Lift
+template <int FMT>
+__device__ __forceinline__ bool mx_lifted(uint32_t u) { return FMT == kMXFP8 && u < kMx8Lift; }
 
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }

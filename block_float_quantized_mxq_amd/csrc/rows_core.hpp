@@ -22,7 +22,9 @@
 // a 32-element block, NVFP4 = two 16-element blocks (two E4M3 bytes).  An
 // 8-byte chunk is used for NVFP4 rows whose byte length is not a multiple of 16.
 // MX block scales are powers of two and go into the scaled conversion itself
-// (the decoded bf16 value q * 2^(u-127) is exact wherever it is a normal bf16);
+// (the decoded bf16 value q * 2^(u-127) is exact at every scale byte, with
+// MXFP8 blocks of bytes below kMx8Lift decoded 2^3 larger and scaled back on
+// their fp32 partial sum);
 // NVFP4's E4M3 block scale multiplies the 16-element block's fp32 partial sum,
 // and its per-tensor scale multiplies the final sum.
 //
@@ -299,6 +301,15 @@ struct RowEngine {
                 xw[b][4 * q + 0] = v[0]; xw[b][4 * q + 1] = v[1]; xw[b][4 * q + 2] = v[2]; xw[b][4 * q + 3] = v[3];
             }
         }
+        // MXFP8 passes holding a block with an E8M0 byte below kMx8Lift take
+        // the lifted form (a branch taken by the whole wave or by none of it)
+        bool lifted = false;
+        if constexpr (FMT == kMXFP8) {
+            bool lo = false;
+#pragma unroll
+            for (int j = 0; j < R; ++j) lo = lo || mx_lifted<FMT>(p.sb[j][0]);
+            lifted = __ballot(lo) != 0;
+        }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             uint32_t wp[CS::NP];
@@ -318,13 +329,27 @@ struct RowEngine {
                     }
                     acc[j][b] = valid ? a : acc[j][b];
                 }
-            } else {
+            } else if (!lifted) {
                 decode_dwords_scaled<FMT, CS::DW>(p.cw[j], e8m0_exponent(p.sb[j][0]), wp);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     float a = acc[j][b];
 #pragma unroll
                     for (int t = 0; t < CS::NP; ++t) a = dot2_bf16(wp[t], xw[b][t], a);
+                    acc[j][b] = valid ? a : acc[j][b];
+                }
+            } else {
+                // a lifted MXFP8 chunk: decoded 2^3 larger, its partial sum scaled back in fp32
+                const uint32_t u = p.sb[j][0];
+                const bool lo = mx_lifted<FMT>(u);
+                decode_dwords_scaled<FMT, CS::DW>(p.cw[j], e8m0_exponent(lo ? u + kMx8Lift : u), wp);
+                const float mul = lo ? kMx8Unlift : 1.0f;
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < CS::NP; ++t) part = dot2_bf16(wp[t], xw[b][t], part);
+                    const float a = __builtin_fmaf(part, mul, acc[j][b]);
                     acc[j][b] = valid ? a : acc[j][b];
                 }
             }

@@ -133,10 +133,12 @@ mxq_status_t mxq_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, 
  *
  * W is decoded to bf16 tiles and multiplied on the bf16 matrix cores with fp32
  * accumulation; the NVFP4 per-tensor scale multiplies the fp32 result.  The
- * decoded tile is exact whenever each weight is zero or a normal bf16: for
- * any code that holds for E8M0 bytes in [2, 252] (MXFP4) and [10, 246]
- * (MXFP8, whose smallest subnormal is 2^-9), and always for NVFP4 (q * s has
- * at most 6 significant bits and lies in [2^-10, 2688]).
+ * decode is exact for every code at every scale byte: an E2M1 value times an
+ * E8M0 scale is always a bf16 (subnormal, infinite or NaN included), so is an
+ * E4M3 value at E8M0 bytes >= 3, and NVFP4's q * s has at most 6 significant
+ * bits.  MXFP8 blocks with an E8M0 byte of 0, 1 or 2 (values finer than bf16's
+ * smallest subnormal) are decoded 2^3 larger and their fp32 contribution is
+ * multiplied by 2^-3, which is exact.
  *   x       bf16 [m][k]
  *   y       [m][n], fp32 (y_dtype MXQ_OUT_F32) or bf16 rounded to nearest even
  *           from the fp32 result (MXQ_OUT_BF16)
@@ -149,8 +151,11 @@ mxq_status_t mxq_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, cons
  * Decoded weights, for checking the in-kernel decode bit for bit:
  *   w[r][j] = fl32(q * 2^(u-127))        MX formats
  *   w[r][j] = fl32((q * s) * g)          NVFP4 (q*s is exact; one rounding)
- * with q the decoded code, u the E8M0 byte, s the decoded E4M3 block scale and
- * g the per-tensor scale.  Uses the same device decode as the other kernels.
+ * with q the decoded code, u the E8M0 byte (255: NaN), s the decoded E4M3
+ * block scale and g the per-tensor scale.  It runs the decode of the product
+ * kernels: the scaled conversion with the E8M0 byte as its scale (MXFP8 bytes
+ * 0..2 lifted by 2^3 and scaled back in fp32), or the unit-scale conversion
+ * times s (NVFP4); the result is exact for every code and every scale byte.
  *   w   fp32 [rows][k]
  */
 mxq_status_t mxq_dequant(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,

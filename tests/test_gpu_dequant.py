@@ -1,7 +1,8 @@
-"""In-kernel decode, bit for bit: mxq_dequant (the same register decode the
-GEMV, MoE and GEMM kernels use) against the oracle's fp32 decode, over every
-code x every scale byte of each format, including subnormal, overflow and NaN
-scales."""
+"""In-kernel decode, bit for bit: mxq_dequant (the scaled-conversion decode the
+GEMV, MoE and GEMM kernels run, with the same MXFP8 lift for E8M0 bytes below
+3) against the oracle's fp32 decode, over every code x every scale byte of each
+format, including subnormal, overflow and NaN scales.  The product kernels
+themselves are checked through one-hot activations in test_gpu_decode_paths."""
 import numpy as np
 import pytest
 
