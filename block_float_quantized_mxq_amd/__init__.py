@@ -52,10 +52,11 @@ def lib() -> ctypes.CDLL:
         L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+        L.mxq_moe_block_noalloc.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
-                  L.mxq_moe_gemm, L.mxq_quantize):
+                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -185,10 +186,12 @@ def moe_route(logits, topk, renorm=False, ids=None, weights=None, stream=None):
 
 
 def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights, x, gu_global_scale=None,
-              dn_global_scale=None, h=None, out=None, stream=None):
+              dn_global_scale=None, h=None, out=None, stream=None, noalloc=False):
     """MoE decode block -> float32 [tokens, hidden]: y[t] = sum_s w[t][s] * W_dn[e] . bf16(silu(gate) * up),
     with gate/up = W_gu[e] . x[t] (rows [0, dff) and [dff, 2 dff) of the gate/up bank).
-    h is the float32 [tokens, topk, 2 dff] workspace (allocated when None)."""
+    h is the float32 [tokens, topk, 2 dff] workspace (allocated when None).  With noalloc the call goes to
+    mxq_moe_block_noalloc, whose workspace is the library's static device array (h must be None; `out`
+    is still allocated here when None)."""
     gu_codes = _dev(gu_codes, torch.uint8, "gu_codes")
     gu_scales = _dev(gu_scales, torch.uint8, "gu_scales")
     dn_codes = _dev(dn_codes, torch.uint8, "dn_codes")
@@ -208,16 +211,27 @@ def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights
     tokens, topk = expert_ids.shape
     if tuple(x.shape) != (tokens, hidden):
         raise ValueError(f"x must have shape {(tokens, hidden)}, got {tuple(x.shape)}")
-    if h is None:
-        h = torch.empty((tokens, topk, 2 * dff), dtype=torch.float32, device=gu_codes.device)
-    h = _dev(h, torch.float32, "h")
-    if h.numel() < tokens * topk * 2 * dff:
-        raise ValueError("h must hold tokens * topk * 2 * dff elements")
+    if noalloc:
+        if h is not None:
+            raise ValueError("noalloc takes no workspace")
+    else:
+        if h is None:
+            h = torch.empty((tokens, topk, 2 * dff), dtype=torch.float32, device=gu_codes.device)
+        h = _dev(h, torch.float32, "h")
+        if h.numel() < tokens * topk * 2 * dff:
+            raise ValueError("h must hold tokens * topk * 2 * dff elements")
     if out is None:
         out = torch.empty((tokens, hidden), dtype=torch.float32, device=gu_codes.device)
     out = _dev(out, torch.float32, "out")
     if out.numel() != tokens * hidden:
         raise ValueError("out must hold tokens * hidden elements")
+    if noalloc:
+        _check(lib().mxq_moe_block_noalloc(fmt, _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global_scale),
+                                           _ptr(dn_codes), _ptr(dn_scales), _ptr(dn_global_scale), _ptr(expert_ids),
+                                           _ptr(weights), _ptr(x), _ptr(out), experts, hidden, dff, tokens, topk,
+                                           _stream(stream)),
+               "mxq_moe_block_noalloc")
+        return out
     _check(lib().mxq_moe_block(fmt, _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global_scale), _ptr(dn_codes),
                                _ptr(dn_scales), _ptr(dn_global_scale), _ptr(expert_ids), _ptr(weights), _ptr(x),
                                _ptr(h), _ptr(out), experts, hidden, dff, tokens, topk, _stream(stream)),

@@ -127,7 +127,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 3; }
+MXQ_API int mxq_abi_version(void) { return 4; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -266,15 +266,19 @@ MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* 
     return launched(mxq::launch_moe_gemm(a, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
-                                   const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
-                                   const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h,
-                                   float* y, int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens,
-                                   int64_t topk, void* stream) {
+namespace {
+
+// Validation of the MoE block's arguments, in the order the header lists; the
+// workspace h is checked when need_h (the allocation-free variant has none).
+mxq_status_t check_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
+                             const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
+                             const int32_t* expert_ids, const float* weights, const uint16_t* x, const float* h,
+                             bool need_h, const float* y, int64_t num_experts, int64_t hidden, int64_t dff,
+                             int64_t tokens, int64_t topk) {
     mxq_status_t st = check_weight(fmt, gu_codes, gu_scales, gu_gscale);
     if (st != MXQ_OK) return st;
     if ((st = check_weight(fmt, dn_codes, dn_scales, dn_gscale)) != MXQ_OK) return st;
-    if (!expert_ids || !weights || !x || !h || !y) return MXQ_E_NULLPTR;
+    if (!expert_ids || !weights || !x || (need_h && !h) || !y) return MXQ_E_NULLPTR;
     if (num_experts <= 0 || tokens <= 0 || topk <= 0) return MXQ_E_SHAPE;
     if ((st = check_k(fmt, hidden)) != MXQ_OK) return st;
     if ((st = check_k(fmt, dff)) != MXQ_OK) return st;
@@ -285,12 +289,56 @@ MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8
         return MXQ_E_UNSUPPORTED;
     const int64_t slots = topk <= 1 ? 1 : topk <= 2 ? 2 : topk <= 4 ? 4 : topk <= 8 ? 8 : 16;
     if (slots * dff * 2 > mxq::kMoeBlockMaxLds) return MXQ_E_UNSUPPORTED;
-    int cus = 0;
-    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    return MXQ_OK;
+}
+
+// The block's two kernels on validated arguments, with the gate/up outputs in h.
+mxq_status_t run_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
+                           const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
+                           const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h, float* y,
+                           int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk, int cus,
+                           void* stream) {
+    mxq_status_t st;
     const mxq::MoeArgs gu{fmt, gu_codes, gu_scales, gu_gscale, expert_ids, x, 0, h, num_experts, 2 * dff, hidden,
                           tokens, topk, cus};
     if ((st = launched(mxq::launch_moe(gu, as_stream(stream)))) != MXQ_OK) return st;
     const mxq::MoeBlockArgs dn{fmt, dn_codes, dn_scales, dn_gscale, expert_ids, weights, h, y, num_experts, hidden, dff,
                                tokens, topk};
     return launched(mxq::launch_moe_down(dn, as_stream(stream)));
+}
+
+}  // namespace
+
+MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
+                                   const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
+                                   const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h,
+                                   float* y, int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens,
+                                   int64_t topk, void* stream) {
+    mxq_status_t st = check_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids,
+                                      weights, x, h, true, y, num_experts, hidden, dff, tokens, topk);
+    if (st != MXQ_OK) return st;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    return run_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids, weights, x, h,
+                         y, num_experts, hidden, dff, tokens, topk, cus, stream);
+}
+
+MXQ_API mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                                           const float* gu_gscale, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                                           const float* dn_gscale, const int32_t* expert_ids, const float* weights,
+                                           const uint16_t* x, float* y, int64_t num_experts, int64_t hidden,
+                                           int64_t dff, int64_t tokens, int64_t topk, void* stream) {
+    mxq_status_t st = check_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids,
+                                      weights, x, nullptr, false, y, num_experts, hidden, dff, tokens, topk);
+    if (st != MXQ_OK) return st;
+    if (tokens * topk * 2 * dff * (int64_t)sizeof(float) > mxq::kMoeBlockScratchBytes) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    float* h = nullptr;
+    if (mxq::moe_block_scratch(&h) != hipSuccess || !h) {
+        (void)hipGetLastError();
+        return MXQ_E_DEVICE;
+    }
+    return run_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids, weights, x, h,
+                         y, num_experts, hidden, dff, tokens, topk, cus, stream);
 }

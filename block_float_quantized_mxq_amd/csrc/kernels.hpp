@@ -102,6 +102,14 @@ struct MoeBlockArgs {
 // power of two, dff bf16 each).
 constexpr int64_t kMoeBlockMaxLds = 64 * 1024;
 
+// Allocation-free MoE block: the gate/up outputs h (fp32 [tokens][topk][2 dff])
+// live in a static device array of this many bytes, one per GPU.  Every call
+// the LDS budget admits fits (topk * dff <= 32768 and tokens <= 8 give at most
+// 2 MiB).
+constexpr int64_t kMoeBlockScratchBytes = int64_t(2) << 20;
+// The array's device address on the current device (looked up once per device).
+hipError_t moe_block_scratch(float** ptr);
+
 // Expert-batched MoE GEMM: Y[q][:] = W[ids[q]] . X[q / topk] (or X[q] with
 // x_per_slot) for the pairs q = token * topk + slot; workspace = goff[experts
 // + 1] then gperm[m * topk].

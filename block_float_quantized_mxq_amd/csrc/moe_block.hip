@@ -23,6 +23,7 @@
 // depend on how the softmax is rounded; the weights are the softmax
 // probabilities of the selected experts, optionally renormalised over them.
 #include <cstdlib>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "rows_core.hpp"
@@ -284,6 +285,38 @@ bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st) {
                                                                  : launch_down_cb<kNVFP4, 8>(a, st);
     }
     return false;
+}
+
+// ---- workspace of the allocation-free entry point -----------------------------------
+
+// The gate/up outputs of mxq_moe_block_noalloc.  Host code never uses this
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, and is cached below.  Every call on a device shares the
+// array; h is written in full by the gate/up kernel before the down kernel
+// reads it, so nothing needs clearing, and calls that overlap on one device
+// (different streams) race on it.
+static __device__ __align__(256) float scratch[kMoeBlockScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t moe_block_scratch(float** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 }  // namespace mxq

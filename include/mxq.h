@@ -210,6 +210,27 @@ mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_s
                            void *stream);
 
 /*
+ * Allocation-free MoE decode block, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, kernels and arguments as
+ * mxq_moe_block without `h`; the gate/up outputs go to a static device array
+ * of 2 MiB that the library holds on each GPU it runs on until the process
+ * ends (looked up once per device; the call allocates nothing).
+ *   tokens * topk * 2 * dff * 4 bytes at most 2 MiB (every call the LDS limit
+ *   above admits fits), else MXQ_E_UNSUPPORTED; MXQ_E_DEVICE if the array's
+ *   address cannot be obtained.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU
+ * (different streams, or several host threads) race and must be serialised
+ * by the caller.  The array needs no clearing (h is written in full before it
+ * is read).
+ */
+mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales,
+                                   const float *gu_gscale, const uint8_t *dn_codes, const uint8_t *dn_scales,
+                                   const float *dn_gscale, const int32_t *expert_ids, const float *weights,
+                                   const uint16_t *x, float *y, int64_t num_experts, int64_t hidden, int64_t dff,
+                                   int64_t tokens, int64_t topk, void *stream);
+
+/*
  * Expert-batched MoE GEMM (prefill).  The "Decoding block-float formats in
  * software" section of the "MLxcel 0.8 release" post credits a kernel that
  * processes the tokens expert by expert for its MXFP4 MoE prefill gain; here
@@ -264,7 +285,7 @@ mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale,
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 3 (2 plus mxq_moe_gemm and mxq_quantize). */
+/* ABI version of this header: 4 (3 plus mxq_moe_block_noalloc). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus
