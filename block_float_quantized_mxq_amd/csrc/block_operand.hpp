@@ -27,14 +27,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Two E2M1 codes (byte SEL of w) times an arbitrary fp32 scale s, as a bf16 pair.
-template <int SEL>
-__device__ __forceinline__ uint32_t scaled_fp4x2_to_bf16x2(uint32_t w, float s) {
-    const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-    const bf16x2_t b = {(__bf16)(f[0] * s), (__bf16)(f[1] * s)};
-    return __builtin_bit_cast(uint32_t, b);
-}
-
 // One lane's W codes for one slice: the 32 consecutive k of one row starting
 // at a multiple of 32, and their scale byte(s).
 template <int FMT>

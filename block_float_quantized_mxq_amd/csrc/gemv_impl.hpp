@@ -29,15 +29,15 @@ constexpr int64_t kMaxXLds = 72 * 1024;
 // tile, tile + gridDim.x, ... go to one workgroup as one stream of passes, so
 // the GPU sweeps the matrix front to back; the first pass is in flight while
 // the activations are staged.
-template <int FMT, int CB, int B, int G, int S, int R, bool XL>
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool MM>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ gscale,
                                                              const uint16_t* __restrict__ x, float* __restrict__ y,
                                                              int64_t n, int64_t k, int batch, int64_t ntiles) {
     using T = RowTile<G, S, R>;
-    using E = RowEngine<FMT, CB, B, G, S, R, XL>;
-    __shared__ float red[S > 1 ? S * T::ROWSETS * R * B : 1];
+    using E = RowEngine<FMT, CB, B, G, S, R, XL, false, MM>;
+    __shared__ float red[E::RED_FLOATS];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
     const uint16_t* xs[B];
     float* ys[B];
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
     PassRing<typename E::Pass, kGemvAhead + 1> ring;
     eng.template prime<kGemvAhead>(cur, ring);
     const float gmul = (FMT == kNVFP4) ? gscale[0] : 1.0f;
-    if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
+    if constexpr (XL) stage_x<FMT, CB, B, MM>(xs, k, xlds);
     eng.template run<kGemvAhead>(cur, ring, xs, ys, gmul, red, xlds);
 }
 
@@ -74,14 +74,15 @@ static int64_t resident_per_cu(K kernel, size_t lds, std::atomic<int64_t>& cache
     return nb;
 }
 
-template <int FMT, int CB, int B, int G, int S, int R>
+template <int FMT, int CB, int B, int G, int S, int R, bool MM = false>
 static void launch_rows_inst(const GemvArgs& a, int64_t per_cu, int grid_mode, hipStream_t st) {
     using T = RowTile<G, S, R>;
     static std::atomic<int64_t> occ_cache[2] = {{-1}, {-1}};
     const int64_t ntiles = (a.n + T::ROWS - 1) / T::ROWS;
     const bool xl = x_lds_bytes<FMT, CB>(a.k, B) <= kMaxXLds;
     const size_t lds = xl ? (size_t)x_lds_bytes<FMT, CB>(a.k, B) : 0;
-    const auto kernel = xl ? gemv_rows_kernel<FMT, CB, B, G, S, R, true> : gemv_rows_kernel<FMT, CB, B, G, S, R, false>;
+    const auto kernel = xl ? gemv_rows_kernel<FMT, CB, B, G, S, R, true, MM>
+                           : gemv_rows_kernel<FMT, CB, B, G, S, R, false, MM>;
     // Stay resident: no more workgroups per CU than fit at once.
     const int64_t fit = resident_per_cu(kernel, lds, occ_cache[xl ? 1 : 0]);
     if (per_cu > fit) per_cu = fit;
@@ -136,11 +137,45 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
     return false;
 }
 
+// Matrix-mode settings (k split across waves s, four-row groups per lane r).
+#define MXQ_MM_SHAPES(X) X(1, 4) X(2, 4) X(4, 4) X(2, 2) X(4, 2)
+
+// Matrix mode (rows_core.hpp, MM) for batches 2 .. 4.  Settings measured on
+// MI355X over the dense shapes (gate/up 51200 x 5120, down 5120 x 25600, QKV
+// 7168 x 5120): k split across 2 waves, or 4 for rows of 1024 chunks and more;
+// 4 four-row groups per lane from batch 3 on long or many rows, else 2.  Batch
+// 4: gate/up 41.6 -> 27.8 us, down 39.5 -> 23.1 us, QKV 10.9 -> 9.2 us against
+// the FMA mode; batch 2: gate/up 27.6 -> 25.4 us, down 23.8 -> 18.7 us.
+template <int FMT, int CB, int B>
+static bool launch_rows_mm(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
+    int sp = cfg.mfma_ks, r = cfg.mfma_r;
+    const int64_t occ = cfg.mfma_occ > 0 ? cfg.mfma_occ : 8;
+    if (sp == 0) {
+        const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
+        sp = nchunks >= 1024 ? 4 : 2;
+        r = (a.batch >= 3 && (a.n >= 16384 || nchunks >= 1024)) ? 4 : 2;
+    }
+#define MXQ_MM_CASE(S_, R_)                                                    \
+    if (sp == S_ && r == R_) {                                                \
+        launch_rows_inst<FMT, CB, B, 16, S_, R_, true>(a, occ, cfg.rows_grid, st); \
+        return true;                                                          \
+    }
+    MXQ_MM_SHAPES(MXQ_MM_CASE)
+#undef MXQ_MM_CASE
+    return false;
+}
+
 template <int FMT, int CB>
 static bool launch_gemv_cb(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
-    // The FMA path spends one dot2 per two weights per batch entry; from batch
-    // 5 (the 8-vector instance) the matrix unit is faster at every dense
-    // shape measured on MI355X, below it the FMA path is.
+    // Batch 1: the FMA mode (HBM bound, fastest on every dense shape).  Batch
+    // 2 .. 4: matrix mode, where the FMA mode's dot2 per two weights per
+    // vector makes the vector ALU the bound.  From batch 5: the matrix-unit
+    // GEMV (16 vectors per MFMA column set).
+    if (cfg.path == 4 || (cfg.path == 0 && a.batch >= 2 && a.batch <= 4)) {
+        if (a.batch <= 1) return launch_rows_mm<FMT, CB, 1>(a, cfg, st);
+        if (a.batch <= 2) return launch_rows_mm<FMT, CB, 2>(a, cfg, st);
+        if (a.batch <= 4) return launch_rows_mm<FMT, CB, 4>(a, cfg, st);
+    }
     const bool mfma = cfg.path == 1 || (cfg.path == 0 && a.batch >= 5);
     if (mfma && a.k % 32 == 0) return launch_gemv_mfma<FMT>(a, cfg, st);
     if (a.batch <= 1) return launch_rows_b<FMT, CB, 1>(a, cfg, st);

@@ -27,7 +27,9 @@ struct GemvArgs {
 struct GemvConfig {
     int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
     int rows_grid = 0;  // 0: min(tiles, resident); 1: equal tiles per workgroup; 2: one workgroup per tile
-    // Path: 0 = by batch (matrix unit from batch 5), 1 = matrix unit, 2 = FMA rows.
+    // Path: 0 = by batch (FMA rows at batch 1, matrix-mode rows at 2 .. 4,
+    // matrix unit from 5), 1 = matrix unit, 2 = FMA rows, 4 = matrix-mode rows
+    // (batch <= 4; mfma_ks = k split across waves, mfma_r = four-row groups).
     int path = 0;
     // Matrix-unit settings: rows per wave (x16), k split, waves per workgroup,
     // workgroups per CU; mfma_ks == 0 = chosen from the shape.

@@ -100,6 +100,15 @@ constexpr float kMx8Unlift = 0.125f;  // 2^-kMx8Lift
 template <int FMT>
 __device__ __forceinline__ bool mx_lifted(uint32_t u) { return FMT == kMXFP8 && u < kMx8Lift; }
 
+// Two E2M1 codes (byte SEL of w) times an fp32 scale s (an E4M3 block scale),
+// as a bf16 pair: q * s has at most 6 significant bits, so the bf16 is exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t scaled_fp4x2_to_bf16x2(uint32_t w, float s) {
+    const f32x2_t f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+    const bf16x2_t b = {(__bf16)(f[0] * s), (__bf16)(f[1] * s)};
+    return __builtin_bit_cast(uint32_t, b);
+}
+
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
 

@@ -137,9 +137,10 @@ struct RowTile {
     static constexpr int ROWS = ROWSETS * R;  // rows per workgroup
 };
 
-// Copies x[B][k] into LDS (layout above).  Every thread of the workgroup must
-// call it; it ends with a barrier.
-template <int FMT, int CB, int B>
+// Copies x[B][k] into LDS (layout above; with MM the flat chunk index is
+// v = c * B + b instead, batch entries of one chunk side by side).  Every
+// thread of the workgroup must call it; it ends with a barrier.
+template <int FMT, int CB, int B, bool MM = false>
 __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t k, uint8_t* xlds) {
     using CS = ChunkShape<FMT, CB>;
     constexpr int U = 8;  // pieces per thread in flight
@@ -147,7 +148,7 @@ __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t 
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const u32x4_t* src = reinterpret_cast<const u32x4_t*>(xs[b]);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xlds) + (int64_t)b * pieces;
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xlds);
         for (int64_t t0 = threadIdx.x; t0 < pieces; t0 += U * kThreads) {
             u32x4_t v[U];
 #pragma unroll
@@ -161,8 +162,8 @@ __device__ __forceinline__ void stage_x(const uint16_t* const (&xs)[B], int64_t 
                 if (t < pieces) {
                     const int64_t c = t / CS::XQ;
                     const int q = (int)(t % CS::XQ);
-                    const int64_t v_flat = (int64_t)b * (pieces / CS::XQ) + c;  // b * nchunks + c
-                    dst[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(v_flat))] = v[u];
+                    const int64_t v_flat = MM ? c * B + b : (int64_t)b * (pieces / CS::XQ) + c;
+                    dst[v_flat * CS::XQ + (q ^ x_swizzle<FMT, CB>(v_flat))] = v[u];
                 }
             }
         }
@@ -228,28 +229,56 @@ struct RowCursor {
 // all of its own row (the caller points each lane's `codes`/`scales` at its
 // group's matrix), against activation vector s of the staged LDS block (B must
 // be 1), and the S partial sums are combined with per-group multipliers.
-template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool SLOTS = false>
+//
+// With MM (matrix mode, batch up to 4) the contraction runs on the 16 x 16 x 32
+// bf16 MFMA instead of dot2, with the loads of the FMA mode (each wave
+// instruction covers 4 rows x 256 contiguous bytes).  Lane l of a wave holds
+// chunk position 4 * (l / 16) + l % 4 of row (l / 4) % 4 of each of its R
+// four-row groups.  As the A operand, lane l is MFMA row i = l % 16 = 4 * row
+// + segment (segment s = l % 4) and k group l / 16, so MFMA row (row, s) sums
+// the chunks at positions 4g + s.  The B operand's 16 columns are (activation
+// vector v, segment s') = (l / 4 % 4, l % 4): lane l reads vector v at its own
+// chunk, the same positions.  The product then holds, for every row and
+// vector, the sums of the 4 segments on the diagonal blocks s = s' (the other
+// 12 of each 16 are discarded); they are added by one quad reduction at the
+// end of the tile.  The vector ALU only decodes, so batch 4 costs what batch 1
+// does; S splits k across the waves of the workgroup.
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool SLOTS = false, bool MM = false>
 struct RowEngine {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
     using Pass = RowPass<FMT, CB, R>;
     using Rows = RowPtrs<R>;
     using Cursor = RowCursor<R>;
+    static_assert(!MM || (G == 16 && B <= 4 && !SLOTS && (S == 1 || S == 2 || S == 4)),
+                  "matrix mode: 16 chunk positions, batch <= 4, k split across the 4 waves");
+    static constexpr int NA = MM ? 4 : B;  // accumulators per row (MM: the 4 rows of an MFMA block)
+    static constexpr int RED_FLOATS = S > 1 ? S * T::ROWSETS * R * NA : 1;
+    static constexpr int WSETS = 4 / S;    // MM: wave row groups per workgroup
 
     const uint8_t* codes;
     const uint8_t* scales;
     int64_t n, rowbytes, sbytes, nchunks, step, c0, niter;
-    int lane, rs, sp;
+    int lane, rs, sp, mi;
 
     __device__ __forceinline__ RowEngine(const uint8_t* codes_, const uint8_t* scales_, int64_t n_, int64_t k) {
         codes = codes_;
         scales = scales_;
         n = n_;
         const int tid = threadIdx.x;
-        lane = tid % G;
-        const int gid = tid / G;
-        rs = gid / S;
-        sp = gid % S;
+        if constexpr (MM) {
+            const int l = tid & 63;
+            lane = 4 * (l >> 4) + (l & 3);  // chunk position in the 16-chunk window
+            mi = (l >> 2) & 3;              // row within a four-row group; activation vector of the B operand
+            rs = (tid >> 6) / S;            // the wave's row group
+            sp = (tid >> 6) % S;
+        } else {
+            lane = tid % G;
+            const int gid = tid / G;
+            rs = gid / S;
+            sp = gid % S;
+            mi = 0;
+        }
         rowbytes = code_bytes_per_row(FMT, k);
         sbytes = k / CS::BS;
         nchunks = rowbytes / CB;
@@ -264,7 +293,7 @@ struct RowEngine {
     __device__ __forceinline__ void set_rows(Rows& p, int64_t row0) const {
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            int64_t r = row0 + (int64_t)rs * R + j;
+            int64_t r = MM ? row0 + (int64_t)rs * 4 * R + 4 * j + mi : row0 + (int64_t)rs * R + j;
             r = r < n ? r : n - 1;
             p.c[j] = codes + r * rowbytes;
             p.s[j] = scales + r * sbytes;
@@ -283,9 +312,105 @@ struct RowEngine {
         }
     }
 
+    // Pointer i of a small array, by masking (a select chain over the
+    // array's entries is folded back into a dynamically indexed load, which
+    // puts the array in scratch memory).
+    template <class T, int N>
+    static __device__ __forceinline__ T* pick(T* const (&a)[N], int i) {
+        uintptr_t v = 0;
+#pragma unroll
+        for (int k = 0; k < N; ++k) v |= reinterpret_cast<uintptr_t>(a[k]) & (uintptr_t)(-(intptr_t)(i == k));
+        return reinterpret_cast<T*>(v);
+    }
+
+    // Matrix mode: the pass's R chunks through the 16 x 16 x 32 MFMA (see above).
+    __device__ __forceinline__ void compute_mm(const Pass& p, int cv, const uint16_t* const (&xs)[B],
+                                               const uint8_t* xlds, float (&acc)[R][NA]) const {
+        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+        typedef __bf16 bf16x8_mm_t __attribute__((ext_vector_type(8)));
+        constexpr int KSTEPS = CS::NP / 4;  // MFMA k steps (8 elements) per chunk
+        const bool valid = cv < nchunks;
+        const int64_t c = valid ? cv : nchunks - 1;
+        // B operand: activation vector mi at this lane's chunk (zero past the batch or the row)
+        uint32_t xw[CS::NP];
+#pragma unroll
+        for (int t = 0; t < CS::NP; ++t) xw[t] = 0u;
+        if (mi < B && valid) {
+            const int64_t vc = c * B + mi;
+            const u32x4_t* xp = XL ? reinterpret_cast<const u32x4_t*>(xlds) + vc * CS::XQ
+                                   : reinterpret_cast<const u32x4_t*>(pick(xs, mi)) + c * CS::XQ;
+            const int swz = XL ? x_swizzle<FMT, CB>(vc) : 0;
+#pragma unroll
+            for (int q = 0; q < CS::XQ; ++q) {
+                const u32x4_t v = xp[q ^ swz];
+                xw[4 * q + 0] = v[0]; xw[4 * q + 1] = v[1]; xw[4 * q + 2] = v[2]; xw[4 * q + 3] = v[3];
+            }
+        }
+        bf16x8_mm_t bx[KSTEPS];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+            bx[t] = __builtin_bit_cast(bf16x8_mm_t, u32x4_t{xw[4 * t], xw[4 * t + 1], xw[4 * t + 2], xw[4 * t + 3]});
+        bool lifted = false;
+        if constexpr (FMT == kMXFP8) {
+            bool lo = false;
+#pragma unroll
+            for (int j = 0; j < R; ++j) lo = lo || mx_lifted<FMT>(p.sb[j][0]);
+            lifted = __ballot(lo) != 0;
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            // A operand: the decoded chunk of row j (zero past the row end, where
+            // the re-read chunk is not this lane's to add)
+            uint32_t wp[CS::NP];
+            bool lo = false;
+            if constexpr (FMT == kNVFP4) {
+                float sc[CS::NSG];
+                scale_values<FMT, CB>(p.sb[j], sc);
+#pragma unroll
+                for (int d = 0; d < CS::DW; ++d) {
+                    const float sv = sc[(4 * d) / CS::PPS];
+                    wp[4 * d + 0] = scaled_fp4x2_to_bf16x2<0>(p.cw[j][d], sv);
+                    wp[4 * d + 1] = scaled_fp4x2_to_bf16x2<1>(p.cw[j][d], sv);
+                    wp[4 * d + 2] = scaled_fp4x2_to_bf16x2<2>(p.cw[j][d], sv);
+                    wp[4 * d + 3] = scaled_fp4x2_to_bf16x2<3>(p.cw[j][d], sv);
+                }
+            } else {
+                const uint32_t u = p.sb[j][0];
+                lo = mx_lifted<FMT>(u);
+                decode_dwords_scaled<FMT, CS::DW>(p.cw[j], e8m0_exponent(lo ? u + kMx8Lift : u), wp);
+            }
+#pragma unroll
+            for (int t = 0; t < CS::NP; ++t) wp[t] = valid ? wp[t] : 0u;
+            f32x4_t d = {acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+            if (!lifted) {
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t)
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_mm_t, u32x4_t{wp[4 * t], wp[4 * t + 1], wp[4 * t + 2], wp[4 * t + 3]}),
+                        bx[t], d, 0, 0, 0);
+            } else {
+                // lifted MXFP8 rows (decoded 2^3 larger) go into a sum scaled back in fp32
+                f32x4_t e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t) {
+                    const u32x4_t w4 = {wp[4 * t], wp[4 * t + 1], wp[4 * t + 2], wp[4 * t + 3]};
+                    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mm_t, lo ? z4 : w4), bx[t], d, 0, 0, 0);
+                    e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mm_t, lo ? w4 : z4), bx[t], e, 0, 0, 0);
+                }
+                d += e * kMx8Unlift;
+            }
+            acc[j][0] = d[0]; acc[j][1] = d[1]; acc[j][2] = d[2]; acc[j][3] = d[3];
+        }
+    }
+
     // Arithmetic of the pass with chunk cv on its loaded chunks.
     __device__ __forceinline__ void compute(const Pass& p, int cv, const uint16_t* const (&xs)[B],
-                                            const uint8_t* xlds, float (&acc)[R][B]) const {
+                                            const uint8_t* xlds, float (&acc)[R][NA]) const {
+        if constexpr (MM) {
+            compute_mm(p, cv, xs, xlds, acc);
+            return;
+        }
         const bool valid = cv < nchunks;
         const int64_t c = valid ? cv : nchunks - 1;
         uint32_t xw[B][CS::NP];
@@ -360,8 +485,12 @@ struct RowEngine {
     // ys[b][row] = gmul * sum (rows >= n are not written; ys[b] == nullptr
     // skips entry b).  With SLOTS the groups' sums are weighted by smul[s] and
     // groups s >= nslot are left out.
-    __device__ __forceinline__ void finish(int64_t row0, float (&acc)[R][B], float* const (&ys)[B], float gmul,
+    __device__ __forceinline__ void finish(int64_t row0, float (&acc)[R][NA], float* const (&ys)[B], float gmul,
                                            float* red, const float* smul = nullptr, int nslot = S) const {
+        if constexpr (MM) {
+            finish_mm(row0, acc, ys, gmul, red);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
@@ -406,6 +535,56 @@ struct RowEngine {
                             if (ys[b]) ys[b][r] = v * gmul;
                         }
                     }
+                }
+            }
+            lds_barrier();  // `red` is rewritten by the next tile
+        }
+    }
+
+    // Matrix mode: lane l holds the product rows 4q + e (q = l / 16, e = 0..3)
+    // of column l % 16 for each of its R groups; the diagonal entry e = l % 4
+    // is row q's sum over segment l % 4 for activation vector (l / 4) % 4.  A
+    // quad reduction adds the 4 segments (fixed order), then the S waves of a
+    // row group are added through LDS.
+    __device__ __forceinline__ void finish_mm(int64_t row0, float (&acc)[R][NA], float* const (&ys)[B], float gmul,
+                                              float* red) const {
+        const int l = threadIdx.x & 63;
+        const int e = l & 3, q = l >> 4;
+        float v[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            // the lane's diagonal entry (register e), by selects
+            float t = (e == 0 ? acc[j][0] : 0.0f) + (e == 1 ? acc[j][1] : 0.0f);
+            t += (e == 2 ? acc[j][2] : 0.0f) + (e == 3 ? acc[j][3] : 0.0f);
+            t += dpp_f32<kDppQuadXor1>(t);
+            t += dpp_f32<kDppQuadXor2>(t);
+            v[j] = t;
+        }
+        const bool head = e == 0;  // lane (q, vector mi) holds row q's total
+        if constexpr (S == 1) {
+            float* yp = pick(ys, mi);
+            if (head && mi < B && yp) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    const int64_t r = row0 + (int64_t)rs * 4 * R + 4 * j + q;
+                    if (r < n) yp[r] = v[j] * gmul;
+                }
+            }
+        } else {
+            if (head) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) red[((sp * WSETS + rs) * 4 * R + 4 * j + q) * 4 + mi] = v[j];
+            }
+            lds_barrier();
+            for (int t = threadIdx.x; t < WSETS * 4 * R * 4; t += kThreads) {
+                const int vv = t & 3, row = t >> 2;  // row within the tile: group * 4R + 4j + q
+                const int64_t r = row0 + row;
+                float* yp = pick(ys, vv);
+                if (r < n && vv < B && yp) {
+                    float sum = red[row * 4 + vv];
+#pragma unroll
+                    for (int s2 = 1; s2 < S; ++s2) sum += red[(s2 * WSETS * 4 * R + row) * 4 + vv];
+                    yp[r] = sum * gmul;
                 }
             }
             lds_barrier();  // `red` is rewritten by the next tile
@@ -468,11 +647,11 @@ struct RowEngine {
         // compute cursor: tile tc, pass ic, chunk cc
         int64_t tc = 0, ic = 0;
         int cc = (int)c0;
-        float acc[R][B];
+        float acc[R][NA];
 #pragma unroll
         for (int j = 0; j < R; ++j)
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[j][b] = 0.0f;
+            for (int b = 0; b < NA; ++b) acc[j][b] = 0.0f;
         auto arith = [&](const Pass& cur) {
             compute(cur, cc, xs, xlds, acc);
             cc += (int)step;
@@ -481,7 +660,7 @@ struct RowEngine {
 #pragma unroll
                 for (int j = 0; j < R; ++j)
 #pragma unroll
-                    for (int b = 0; b < B; ++b) acc[j][b] = 0.0f;
+                    for (int b = 0; b < NA; ++b) acc[j][b] = 0.0f;
                 ic = 0;
                 cc = (int)c0;
                 ++tc;

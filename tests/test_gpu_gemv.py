@@ -216,6 +216,28 @@ def test_matrix_unit_settings_all_outputs(setting, fmt, n, k, monkeypatch):
                   f"matrix unit {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}")
 
 
+# Matrix-mode rows (4 = path, then four-row groups per lane, k split across waves).
+MM_SETTINGS = ["4,4,1,0,0", "4,4,2,0,0", "4,4,4,0,0", "4,2,2,0,0", "4,2,4,0,0"]
+
+
+@pytest.mark.parametrize("setting", MM_SETTINGS)
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("n,k", [(1000, 5120), (77, 25600), (129, 768), (300, 96), (5, 4112)])
+def test_matrix_mode_settings_all_outputs(setting, fmt, n, k, monkeypatch):
+    """Every compiled matrix-mode setting (16 x 16 x 32 MFMA on the FMA-mode
+    loads), forced for batches 1 .. 4, every output checked: ragged row groups,
+    rows shorter than one pass, NVFP4 rows of 8-byte chunks (k = 4112)."""
+    monkeypatch.setenv("MXQ_GEMV_MFMA", setting)
+    if k % (16 if fmt == 3 else 32):
+        k += 16  # MX formats: whole 32-element blocks
+    sc, ss, sx, _, _ = synth.streams(11 * n + k + fmt)
+    codes, scales, g = synth.weights(fmt, sc, ss, n, k)
+    for batch in (1, 2, 3, 4):
+        x = synth.bf16_normal(sx, (batch, k))
+        check_all(dict(fmt=fmt, codes=codes, scales=scales, g=g, x=x, n=n, k=k),
+                  f"matrix mode {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}")
+
+
 def test_matrix_unit_and_fma_paths_agree_at_batch_one(monkeypatch):
     """The two GEMV paths on the same full-size gate/up input: each within the
     acceptance bound of the oracle on sampled rows."""
