@@ -70,6 +70,7 @@ def _load():
         D = ctypes.c_double
         lib.orc_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, D, D, D, P, P, P]
         lib.orc_quantize.argtypes = [I, P, ctypes.c_float, I64, I64, P, P]
+        lib.orc_requant_fp8.argtypes = [P, P, I64, I64, I64, I64, P, P]
         _lib = lib
     return _lib
 
@@ -217,6 +218,19 @@ def quantize(fmt, x, g, rows, k):
     codes = np.zeros((rows, k if fmt == 2 else k // 2), dtype=np.uint8)
     scales = np.zeros((rows, k // (16 if fmt == 3 else 32)), dtype=np.uint8)
     _load().orc_quantize(fmt, _ptr(x), float(g if g is not None else 1.0), rows, k, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def requant_fp8(codes_in, tile_scales, n, k, bn=128, bk=128):
+    """MXFP8 (codes uint8 [n][k], E8M0 scales uint8 [n][k/32]) of an FP8 block checkpoint: E4M3 codes
+    uint8 [n][k] with one fp32 scale per bn x bk tile, tile_scales float32 [ceil(n/bn)][ceil(k/bk)]."""
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    codes_in = _c(codes_in, np.uint8)
+    tile_scales = _c(tile_scales, np.float32)
+    codes = np.zeros((n, k), dtype=np.uint8)
+    scales = np.zeros((n, k // 32), dtype=np.uint8)
+    _load().orc_requant_fp8(_ptr(codes_in), _ptr(tile_scales), n, k, bn, bk, _ptr(codes), _ptr(scales))
     return codes, scales
 
 

@@ -498,3 +498,55 @@ void orc_quantize(int fmt, const uint16_t *x, float g, int64_t rows, int64_t k, 
         }
     }
 }
+
+/*
+ * FP8 block checkpoint -> MXFP8.  The ROCm status table of the "Build from
+ * source" manual (section "Current status", row "mxfp8, mxfp4 checkpoints")
+ * converts vendor FP8 checkpoints whose weights are E4M3 codes with one fp32
+ * scale per 128 x 128 tile into MXFP8 when a model loads; the pages give no
+ * procedure.  Reading taken: dequantize, then quantize with the OCP MX
+ * conversion:
+ *   v = fl32(E4M3(c) * s_tile)   (the exact product rounded once to fp32)
+ *   per 32-element block of a row: the OCP MX conversion of the fp32 values v,
+ *   the same steps as orc_quantize for MXFP8 (shared exponent floor(log2 amax)
+ *   - 8, clamped to [-127, 127]; elements rounded to the nearest E4M3 value,
+ *   ties to the even code, saturating at 448, sign kept).
+ * The tile of element (r, j) is (r / bn, j / bk); tile scales are row-major
+ * [ceil(n / bn)][ceil(k / bk)].  Inputs are finite (no NaN codes, finite
+ * products).
+ */
+void orc_requant_fp8(const uint8_t *codes_in, const float *tile_scales, int64_t n, int64_t k, int64_t bn, int64_t bk,
+                     uint8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = k / 32;
+    const int64_t tcols = (k + bk - 1) / bk;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            float v[32];
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                const int64_t col = b * 32 + j;
+                const double s = (double)tile_scales[(r / bn) * tcols + col / bk];
+                v[j] = (float)(orc_e4m3(codes_in[r * k + col]) * s); /* exact product, one rounding */
+                const double a = fabs((double)v[j]);
+                if (a > amax) amax = a;
+            }
+            int se = -127;
+            if (amax > 0.0) {
+                int e;
+                (void)frexp(amax, &e);
+                se = (e - 1) - 8;
+                if (se < -127) se = -127;
+                if (se > 127) se = 127;
+            }
+            scales[r * nb + b] = (uint8_t)(se + 127);
+            const double div = ldexp(1.0, se);
+            for (int j = 0; j < 32; ++j) {
+                const double p = (double)v[j] / div; /* exact: div = 2^se */
+                const unsigned neg = signbit(v[j]) ? 1u : 0u;
+                codes[r * k + b * 32 + j] = (uint8_t)(orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)) | (neg << 7));
+            }
+        }
+    }
+}

@@ -572,6 +572,102 @@ def check_quantize_roundtrip(fmt, seed=17):
     assert (qc == codes).all()
 
 
+# ---- FP8 block checkpoint -> MXFP8 ---------------------------------------------------------
+# Independent reference: torch's E4M3 decoder, the tile scale applied by one numpy float32
+# multiplication, then the MX steps of _quantize_reference on the fp32 values.
+
+def _requant_reference(codes_in, tile_scales, n, k, bn, bk):
+    q = torch.from_numpy(codes_in.copy()).view(torch.float8_e4m3fn).float().numpy()
+    tr, tc = np.arange(n)[:, None] // bn, np.arange(k)[None, :] // bk
+    v = (q * tile_scales[tr, tc]).astype(np.float32)          # float32 product: one rounding
+    e4m3 = _grid("e4m3")
+    codes = np.zeros((n, k), dtype=np.uint8)
+    scales = np.zeros((n, k // 32), dtype=np.uint8)
+    for r in range(n):
+        for b in range(k // 32):
+            blk = v[r, b * 32:(b + 1) * 32].astype(np.float64)
+            amax = float(np.max(np.abs(blk)))
+            se = -127 if amax == 0 else min(127, max(-127, math.frexp(amax)[1] - 1 - 8))
+            scales[r, b] = se + 127
+            for j, val in enumerate(blk):
+                neg = 1 if np.signbit(val) else 0
+                codes[r, b * 32 + j] = _nearest(abs(val) / 2.0 ** se, e4m3) | (neg << 7)
+    return codes, scales
+
+
+def _finite_e4m3(rng, shape, lo=0, hi=15):
+    """Random E4M3 bytes with exponent field in [lo, hi], any sign and mantissa, never NaN."""
+    pool = np.array([c for c in range(256) if lo <= (c >> 3) & 15 <= hi and (c & 0x7F) != 0x7F], dtype=np.uint8)
+    return pool[rng.integers(0, pool.size, size=shape)]
+
+
+def _requant_tie_case(count=24):
+    """Blocks where the fp32 rounding of the dequantized value decides the E4M3 code:
+    q * s (exact) lies just above a midpoint m of two E4M3 values whose lower one has the
+    even code, and fl32(q * s) == m, which then rounds down (ties to even) while the
+    exact product rounds up.  Each 32-block: 256 (sets the MX scale to 2^0 for s in
+    [1, 2)) and 31 copies of q, with its own tile scale s (bn = 1, bk = 32)."""
+    from fractions import Fraction as Fr
+    grid = sorted((v, c) for v, c in _grid("e4m3") if v > 0)
+    rows = []
+    for (lo, clo), (hi, _) in zip(grid, grid[1:]):
+        m = (lo + hi) / 2
+        if clo % 2 or not 1.0 <= m <= 400.0:
+            continue
+        for q, cq in grid:
+            if q < 1.0 or not 1 <= Fr(m) / Fr(q) < 2:
+                continue
+            s32 = np.float32(float(Fr(m) / Fr(q)))
+            if Fr(float(s32)) <= Fr(m) / Fr(q):
+                s32 = np.nextafter(s32, np.float32(2))
+            exact = Fr(float(s32)) * Fr(q)
+            if exact > Fr(m) and Fr(float(np.float32(float(exact)))) == Fr(m):
+                rows.append((float(s32), cq))
+                break
+        if len(rows) >= count:
+            break
+    assert len(rows) >= 8
+    codes = np.array([[0x78] + [cq] * 31 for _, cq in rows], dtype=np.uint8)
+    ts = np.array([[s] for s, _ in rows], dtype=np.float32)
+    return codes, ts
+
+
+def check_requant_nearest(seed=23):
+    rng = np.random.default_rng(seed)
+    codes, ts = _requant_tie_case()
+    n = codes.shape[0]
+    c, sc = oracle.requant_fp8(codes, ts, n, 32, 1, 32)
+    rc, rs = _requant_reference(codes, ts, n, 32, 1, 32)
+    assert (sc == rs).all() and (c == rc).all(), "fp32 rounding of the dequantized values"
+    for n, k, bn, bk in ((70, 288, 32, 128), (40, 96, 64, 32), (3, 32, 1, 32)):
+        codes = _finite_e4m3(rng, (n, k))
+        tiles = (-(-n // bn), -(-k // bk))
+        ts = (rng.standard_normal(tiles) * np.exp2(rng.integers(-30, 30, size=tiles))).astype(np.float32)
+        ts.flat[0] = np.float32(2.0 ** -7)                       # a power of two among them
+        codes[0, :32] = 0x80                                     # a block of negative zeros
+        codes[1, :32] = _finite_e4m3(rng, 32, 0, 0)              # a block of E4M3 subnormals
+        c, sc = oracle.requant_fp8(codes, ts, n, k, bn, bk)
+        rc, rs = _requant_reference(codes, ts, n, k, bn, bk)
+        assert (sc == rs).all(), (n, k, bn, bk, np.argwhere(sc != rs)[:3])
+        assert (c == rc).all(), (n, k, bn, bk, np.argwhere(c != rc)[:3])
+
+
+def check_requant_roundtrip(seed=29):
+    """Tile scales 2^t (a different t per tile) and every 32-block holding a value of
+    exponent field 15 and only normal values: the MX scale is exactly the tile scale
+    (byte t + 127) and the codes come back unchanged."""
+    rng = np.random.default_rng(seed)
+    n, k, bn, bk = 96, 384, 64, 128
+    codes = _finite_e4m3(rng, (n, k), 1, 15)
+    codes[:, ::32] = rng.choice([0x78, 0x7A, 0x7E, 0xF9, 0xFE], size=(n, k // 32))   # 256 .. 448, either sign
+    t = rng.integers(-20, 10, size=(2, 3))
+    ts = np.exp2(t).astype(np.float32)
+    c, sc = oracle.requant_fp8(codes, ts, n, k, bn, bk)
+    assert (c == codes).all()
+    want = (t[np.arange(n)[:, None] // bn, (np.arange(k // 32)[None, :] * 32) // bk] + 127)
+    assert (sc == want).all()
+
+
 def all_checks():
     """(name, callable) for every pin, used by the mutation test."""
     out = [("e2m1_table", check_e2m1_table), ("e8m0", check_e8m0), ("e4m3", check_e4m3),
@@ -590,5 +686,6 @@ def all_checks():
     out += [(f"quantize_nearest_{f}", lambda f=f: check_quantize_nearest(f)) for f in FMTS]
     out += [("quantize_scale_closed_form", check_quantize_scale_closed_form),
             ("quantize_roundtrip_mxfp4", lambda: check_quantize_roundtrip(MXFP4)),
-            ("quantize_roundtrip_mxfp8", lambda: check_quantize_roundtrip(MXFP8))]
+            ("quantize_roundtrip_mxfp8", lambda: check_quantize_roundtrip(MXFP8)),
+            ("requant_nearest", check_requant_nearest), ("requant_roundtrip", check_requant_roundtrip)]
     return out

@@ -50,6 +50,22 @@ MUTANTS = {
     "block_weight_dropped": ("acc += ws * part;", "acc += part;"),
     "block_no_bf16": ("a[s * dff + j] = orc_round_bf16(p);", "a[s * dff + j] = p;"),
     "block_fp64_swiglu": ("const double p = (double)(float)(s32 * u32);", "const double p = orc_silu(g32) * u32;"),
+    "requant_tile_col": ("tile_scales[(r / bn) * tcols + col / bk]", "tile_scales[(r / bn) * tcols + col / bn]"),
+    "requant_tile_row": ("tile_scales[(r / bn) * tcols + col / bk]", "tile_scales[(r / bk) * tcols + col / bk]"),
+    "requant_scale_dropped": ("v[j] = (float)(orc_e4m3(codes_in[r * k + col]) * s);",
+                              "v[j] = (float)(orc_e4m3(codes_in[r * k + col]));"),
+    "requant_fp64_value": ("float v[32];\n            double amax = 0.0;\n            for (int j = 0; j < 32; ++j) {\n"
+                           "                const int64_t col = b * 32 + j;\n"
+                           "                const double s = (double)tile_scales[(r / bn) * tcols + col / bk];\n"
+                           "                v[j] = (float)(orc_e4m3(codes_in[r * k + col]) * s);",
+                           "double v[32];\n            double amax = 0.0;\n            for (int j = 0; j < 32; ++j) {\n"
+                           "                const int64_t col = b * 32 + j;\n"
+                           "                const double s = (double)tile_scales[(r / bn) * tcols + col / bk];\n"
+                           "                v[j] = (orc_e4m3(codes_in[r * k + col]) * s);"),
+    "requant_emax": ("se = (e - 1) - 8;\n                if (se < -127) se = -127;\n                if (se > 127) se = 127;\n            }\n            scales[r * nb + b]",
+                     "se = (e - 1) - 7;\n                if (se < -127) se = -127;\n                if (se > 127) se = 127;\n            }\n            scales[r * nb + b]"),
+    "requant_sign": ("(uint8_t)(orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)) | (neg << 7));",
+                     "(uint8_t)(orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)));"),
 }
 
 
@@ -72,7 +88,7 @@ def test_pins_reject_mutant(tmp_path, monkeypatch, name):
     mutant = ctypes.CDLL(path)
     for attr in ("orc_e2m1", "orc_e8m0", "orc_e4m3", "orc_bf16", "orc_num_threads", "orc_set_num_threads",
                  "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows", "orc_moe_route", "orc_silu",
-                 "orc_round_bf16", "orc_moe_block", "orc_quantize"):
+                 "orc_round_bf16", "orc_moe_block", "orc_quantize", "orc_requant_fp8"):
         fr, fm = getattr(real, attr), getattr(mutant, attr)
         fm.argtypes, fm.restype = fr.argtypes, fr.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
