@@ -55,8 +55,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_block_noalloc.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
+        L.mxq_requant_fp8.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
         for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
-                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize):
+                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -316,6 +317,30 @@ def quantize(fmt, x, global_scale=None, codes=None, scales=None, stream=None):
         raise ValueError("codes / scales do not match x")
     _check(lib().mxq_quantize(fmt, _ptr(x), _ptr(global_scale), _ptr(codes), _ptr(scales), rows, k,
                               _stream(stream)), "mxq_quantize")
+    return codes, scales
+
+
+def requant_fp8(codes_in, tile_scales, block_n=128, block_k=128, codes=None, scales=None, stream=None):
+    """FP8 block checkpoint -> MXFP8: E4M3 codes uint8 [n, k] with float32 tile scales
+    [ceil(n / block_n), ceil(k / block_k)] -> (codes uint8 [n, k], E8M0 scales uint8 [n, k / 32])."""
+    codes_in = _dev(codes_in, torch.uint8, "codes_in")
+    tile_scales = _dev(tile_scales, torch.float32, "tile_scales")
+    if codes_in.dim() != 2:
+        raise ValueError("codes_in must be [n, k]")
+    n, k = codes_in.shape
+    want = ((n + block_n - 1) // block_n, (k + block_k - 1) // block_k)
+    if tuple(tile_scales.shape) != want:
+        raise ValueError(f"tile_scales must have shape {want}, got {tuple(tile_scales.shape)}")
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.uint8, device=codes_in.device)
+    if scales is None:
+        scales = torch.empty((n, k // 32), dtype=torch.uint8, device=codes_in.device)
+    codes = _dev(codes, torch.uint8, "codes")
+    scales = _dev(scales, torch.uint8, "scales")
+    if codes.numel() != n * k or scales.numel() != n * (k // 32):
+        raise ValueError("codes / scales do not match codes_in")
+    _check(lib().mxq_requant_fp8(_ptr(codes_in), _ptr(tile_scales), _ptr(codes), _ptr(scales), n, k, block_n, block_k,
+                                 _stream(stream)), "mxq_requant_fp8")
     return codes, scales
 
 

@@ -127,7 +127,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 4; }
+MXQ_API int mxq_abi_version(void) { return 5; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -242,6 +242,20 @@ MXQ_API mxq_status_t mxq_quantize(int fmt, const uint16_t* x, const float* globa
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::QuantizeArgs a{fmt, x, global_scale, codes, scales, rows, k};
     return launched(mxq::launch_quantize(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_requant_fp8(const uint8_t* codes_in, const float* tile_scales, uint8_t* codes,
+                                     uint8_t* scales, int64_t n, int64_t k, int64_t block_n, int64_t block_k,
+                                     void* stream) {
+    if (!codes_in || !tile_scales || !codes || !scales) return MXQ_E_NULLPTR;
+    if (n <= 0 || k <= 0 || block_n <= 0 || block_k <= 0 || k % 32 != 0 || block_k % 32 != 0) return MXQ_E_SHAPE;
+    if (!aligned(codes_in, 16) || !aligned(codes, 16) || !aligned(tile_scales, 4)) return MXQ_E_ALIGN;
+    if (n > kMaxDim || k > kMaxDim || n * k > mxq::kMaxQuantizeElems) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    mxq_status_t st;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const mxq::RequantArgs a{codes_in, tile_scales, codes, scales, n, k, block_n, block_k};
+    return launched(mxq::launch_requant_fp8(a, as_stream(stream)));
 }
 
 MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,

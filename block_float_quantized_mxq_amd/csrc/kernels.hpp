@@ -146,6 +146,16 @@ struct QuantizeArgs {
 constexpr int64_t kMaxQuantizeElems = int64_t(1) << 36;
 
 bool launch_quantize(const QuantizeArgs& a, hipStream_t st);
+
+// FP8 block checkpoint (E4M3 codes [n][k], fp32 scale per bn x bk tile) -> MXFP8.
+struct RequantArgs {
+    const uint8_t* codes_in;
+    const float* tile_scales;
+    uint8_t* codes;
+    uint8_t* scales;
+    int64_t n, k, bn, bk;
+};
+bool launch_requant_fp8(const RequantArgs& a, hipStream_t st);
 bool launch_moe_route(const RouteArgs& a, hipStream_t st);
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st);
 bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st);

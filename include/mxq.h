@@ -282,10 +282,32 @@ mxq_status_t mxq_moe_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, 
 mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale, uint8_t *codes, uint8_t *scales,
                           int64_t rows, int64_t k, void *stream);
 
+/*
+ * FP8 block checkpoint -> MXFP8.  The ROCm status table of the "Build from
+ * source" manual (section "Current status", row "mxfp8, mxfp4 checkpoints")
+ * converts vendor FP8 checkpoints to MXFP8 when a model loads; such a
+ * checkpoint stores E4M3 codes with one fp32 scale per 128 x 128 tile.  The
+ * pages give no procedure; the conversion dequantizes and requantizes:
+ *   v = fl32(E4M3(c) * s)   s = tile_scales[r / block_n][j / block_k]
+ *   then, per 32-element block of a row, the OCP MX conversion of mxq_quantize
+ *   (shared exponent floor(log2 max|v|) - 8, clamped to [-127, 127]; codes =
+ *   the nearest E4M3 values of v / 2^exponent, ties to the even code,
+ *   saturating at 448, sign kept).
+ *   codes_in     E4M3 [n][k], 16-byte aligned; finite values (no 0x7F / 0xFF)
+ *   tile_scales  fp32 [ceil(n / block_n)][ceil(k / block_k)], row-major; the
+ *                products E4M3 * scale must be finite fp32 numbers
+ *   codes        out E4M3 [n][k], 16-byte aligned (may not alias codes_in)
+ *   scales       out E8M0 [n][k / 32]
+ *   k and block_k multiples of 32 (a block never straddles two tiles);
+ *   n * k <= 2^36.  Results for non-finite inputs are unspecified.
+ */
+mxq_status_t mxq_requant_fp8(const uint8_t *codes_in, const float *tile_scales, uint8_t *codes, uint8_t *scales,
+                             int64_t n, int64_t k, int64_t block_n, int64_t block_k, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 4 (3 plus mxq_moe_block_noalloc). */
+/* ABI version of this header: 5 (4 plus mxq_requant_fp8). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
-         "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_status_string", "mxq_abi_version"])
+         "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_status_string",
+         "mxq_abi_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 4
+    assert lib.mxq_abi_version() == 5
 
 
 def test_status_strings():
@@ -180,6 +181,20 @@ def test_unsupported_sizes():
     assert quant(rows=1 << 20, k=(1 << 16) + 32) == UNSUPPORTED and quant(rows=1 << 31) == UNSUPPORTED
 
 
+def requant(ci=A, ts=A, co=A, sc=A, n=4, k=256, bn=128, bk=128):
+    return mxq.lib().mxq_requant_fp8(ci, ts, co, sc, n, k, bn, bk, None)
+
+
+def test_requant_argument_errors():
+    for arg in ("ci", "ts", "co", "sc"):
+        assert requant(**{arg: None}) == NULLPTR, arg
+    for arg in ("n", "k", "bn", "bk"):
+        assert requant(**{arg: 0}) == SHAPE and requant(**{arg: -1}) == SHAPE, arg
+    assert requant(k=48) == SHAPE and requant(bk=48) == SHAPE  # whole 32-element blocks in one tile
+    assert requant(ci=A + 8) == ALIGN and requant(co=A + 4) == ALIGN and requant(ts=A + 2) == ALIGN
+    assert requant(n=1 << 20, k=(1 << 16) + 32) == UNSUPPORTED and requant(n=1 << 31) == UNSUPPORTED
+
+
 def _no_gpu():
     import torch
     return torch.cuda.device_count() == 0
@@ -195,6 +210,7 @@ def test_device_error_without_gpu():
     # the largest workspace every admitted call needs (8 tokens x 16 slots x 2 x 2048 floats) fits the array
     assert block_na() == DEVICE and block_na(T=8, topk=16, dff=2048, E=16) == DEVICE
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
+    assert requant() == DEVICE and requant(n=1 << 20, k=1 << 16, bn=1, bk=32) == DEVICE
 
 
 def test_binding_rejects_cpu_tensors():
