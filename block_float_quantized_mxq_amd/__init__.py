@@ -38,6 +38,12 @@ class MxqError(RuntimeError):
 _lib = None
 
 
+class GemvConfig(ctypes.Structure):
+    """mxq_gemv_config_t: the dense GEMV's kernel and tile, for tests and tuning (0 = chosen from the shape)."""
+    _fields_ = [(f, ctypes.c_int32) for f in ("path", "rows_g", "rows_s", "rows_r", "mm_r", "mm_s", "mfma_r",
+                                               "mfma_ks", "mfma_nw", "per_cu")]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (raises if it has not been built)."""
     global _lib
@@ -47,6 +53,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.mxq_gemv.argtypes = [I, P, P, P, P, P, I64, I64, I64, P]
+        L.mxq_gemv_config.argtypes = [I, P, P, P, P, P, I64, I64, I64, ctypes.POINTER(GemvConfig), P]
         L.mxq_moe_gemv.argtypes = [I, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_gemm.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, P]
         L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
@@ -56,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_requant_fp8.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
-        for f in (L.mxq_gemv, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
+        for f in (L.mxq_gemv, L.mxq_gemv_config, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
                   L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
@@ -119,8 +126,9 @@ def _check_weight(fmt, codes, scales, global_scale, experts=None):
     return k
 
 
-def gemv(fmt, codes, scales, x, global_scale=None, out=None, stream=None):
-    """y[b][i] = sum_k W[i][k] * x[b][k] -> float32 [batch, n]."""
+def gemv(fmt, codes, scales, x, global_scale=None, out=None, stream=None, config=None):
+    """y[b][i] = sum_k W[i][k] * x[b][k] -> float32 [batch, n].  config: a dict of mxq_gemv_config_t
+    fields (the kernel and tile chosen by the caller, through mxq_gemv_config), None for mxq_gemv."""
     codes = _dev(codes, torch.uint8, "codes")
     scales = _dev(scales, torch.uint8, "scales")
     x = _dev(x, torch.bfloat16, "x")
@@ -136,6 +144,11 @@ def gemv(fmt, codes, scales, x, global_scale=None, out=None, stream=None):
     out = _dev(out, torch.float32, "out")
     if out.numel() != batch * n:
         raise ValueError("out must hold batch * n elements")
+    if config is not None:
+        cfg = GemvConfig(**config)
+        _check(lib().mxq_gemv_config(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x2), _ptr(out), n, k,
+                                     batch, ctypes.byref(cfg), _stream(stream)), "mxq_gemv_config")
+        return out
     _check(lib().mxq_gemv(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x2), _ptr(out), n, k, batch,
                           _stream(stream)), "mxq_gemv")
     return out

@@ -5,8 +5,6 @@
 // machines without a GPU as well.  Checks run in the order the header lists
 // (format, null pointers, shapes, alignment, supported sizes, device).
 #include <atomic>
-#include <cstdio>
-#include <cstdlib>
 #include <cstring>
 
 #include "../../include/mxq.h"
@@ -79,39 +77,6 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
-namespace mxq {
-
-// Dense GEMV kernel settings: chosen from the shape by the launcher unless
-// MXQ_GEMV_ROWS="g,s,r,wgs_per_cu[,grid]" or
-// MXQ_GEMV_MFMA="path[,r,ks,waves,wgs_per_cu]" overrides them (used only to
-// compare variants when tuning).
-GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch) {
-    (void)fmt, (void)n, (void)k, (void)batch;
-    GemvConfig c;
-    if (const char* env = std::getenv("MXQ_GEMV_ROWS")) {
-        int g = 0, s = 0, r = 0, occ = 0, grid = 0;
-        if (std::sscanf(env, "%d,%d,%d,%d,%d", &g, &s, &r, &occ, &grid) >= 4) {
-            c.rows_g = g;
-            c.rows_s = s;
-            c.rows_r = r;
-            c.rows_occ = occ;
-            c.rows_grid = grid;
-        }
-    }
-    if (const char* env = std::getenv("MXQ_GEMV_MFMA")) {
-        int path = 0, r = 0, ks = 0, nw = 0, occ = 0;
-        if (std::sscanf(env, "%d,%d,%d,%d,%d", &path, &r, &ks, &nw, &occ) >= 1) {
-            c.path = path;
-            c.mfma_r = r;
-            c.mfma_ks = ks;
-            c.mfma_nw = nw;
-            c.mfma_occ = occ;
-        }
-    }
-    return c;
-}
-
-}  // namespace mxq
 
 MXQ_API const char* mxq_status_string(int s) {
     switch (s) {
@@ -127,7 +92,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 5; }
+MXQ_API int mxq_abi_version(void) { return 6; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -141,7 +106,41 @@ MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scal
     int cus = 0;
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::GemvArgs a{fmt, codes, scales, global_scale, x, y, n, k, batch, cus};
-    return launched(mxq::launch_gemv(a, mxq::choose_gemv_config(fmt, n, k, batch), as_stream(stream)));
+    return launched(mxq::launch_gemv(a, mxq::GemvConfig{}, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_gemv_config(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                                     const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch,
+                                     const mxq_gemv_config_t* config, void* stream) {
+    mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
+    if (st != MXQ_OK) return st;
+    if (!x || !y || !config) return MXQ_E_NULLPTR;
+    if (n <= 0 || batch <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
+    if (n > kMaxDim || k > kMaxDim || batch > MXQ_MAX_BATCH) return MXQ_E_UNSUPPORTED;
+    const mxq_gemv_config_t& c = *config;
+    const int32_t fields[] = {c.rows_g, c.rows_s, c.rows_r, c.mm_r, c.mm_s, c.mfma_r, c.mfma_ks, c.mfma_nw, c.per_cu};
+    for (int32_t f : fields)
+        if (f < 0 || f > 64) return MXQ_E_UNSUPPORTED;
+    if (c.path != 0 && c.path != 1 && c.path != 2 && c.path != 4) return MXQ_E_UNSUPPORTED;
+    if (c.path == 4 && batch > 4) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    mxq::GemvConfig cfg;
+    cfg.path = c.path;
+    cfg.rows_g = c.rows_g;
+    cfg.rows_s = c.rows_s;
+    cfg.rows_r = c.rows_r;
+    cfg.rows_occ = c.per_cu;
+    cfg.mm_r = c.mm_r;
+    cfg.mm_s = c.mm_s;
+    cfg.mfma_r = c.mfma_r;
+    cfg.mfma_ks = c.mfma_ks;
+    cfg.mfma_nw = c.mfma_nw;
+    cfg.mfma_occ = c.per_cu;
+    const mxq::GemvArgs a{fmt, codes, scales, global_scale, x, y, n, k, batch, cus};
+    return launched(mxq::launch_gemv(a, cfg, as_stream(stream)));
 }
 
 MXQ_API mxq_status_t mxq_moe_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
@@ -190,7 +189,7 @@ MXQ_API mxq_status_t mxq_gemm(int fmt, const uint8_t* codes, const uint8_t* scal
             float* ys = reinterpret_cast<float*>(static_cast<uint8_t*>(y) + r0 * n * esz);
             mxq::GemvArgs g{fmt, codes, scales, global_scale, x + r0 * k, ys, n, k, rows, cus};
             g.y_bf16 = y_dtype == MXQ_OUT_BF16 ? 1 : 0;
-            mxq::GemvConfig cfg = mxq::choose_gemv_config(fmt, n, k, rows);
+            mxq::GemvConfig cfg;
             cfg.path = 1;
             if ((st = launched(mxq::launch_gemv(g, cfg, as_stream(stream)))) != MXQ_OK) return st;
         }

@@ -148,9 +148,9 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
 // the FMA mode; batch 2: gate/up 27.6 -> 25.4 us, down 23.8 -> 18.7 us.
 template <int FMT, int CB, int B>
 static bool launch_rows_mm(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
-    int sp = cfg.mfma_ks, r = cfg.mfma_r;
-    const int64_t occ = cfg.mfma_occ > 0 ? cfg.mfma_occ : 8;
-    if (sp == 0) {
+    int sp = cfg.mm_s, r = cfg.mm_r;
+    const int64_t occ = cfg.rows_occ > 0 ? cfg.rows_occ : 8;
+    if (sp == 0 || r == 0) {
         const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
         sp = nchunks >= 1024 ? 4 : 2;
         r = (a.batch >= 3 && (a.n >= 16384 || nchunks >= 1024)) ? 4 : 2;

@@ -21,18 +21,21 @@ struct GemvArgs {
     int y_bf16 = 0;  // matrix-unit path only: y holds bf16 (RNE), not fp32
 };
 
-// Dense GEMV settings: lanes per row (rows_g), k split (rows_s), rows per lane
-// (rows_r) and workgroups per CU (rows_occ); 0 = chosen from the shape.  The
-// compiled (g, s, r) combinations are listed in MXQ_ROWS_SHAPES.
+// Dense GEMV settings (0 = chosen from the shape).  FMA rows: lanes per row
+// (rows_g), k split (rows_s), rows per lane (rows_r), workgroups per CU
+// (rows_occ), grid mode (rows_grid); the compiled (g, s, r) combinations are
+// listed in MXQ_ROWS_SHAPES.  Matrix-mode rows: four-row groups per lane
+// (mm_r), k split across waves (mm_s).  Matrix-unit GEMV: row blocks per wave
+// (mfma_r), k split (mfma_ks), waves per workgroup (mfma_nw), workgroups per
+// CU (mfma_occ).  mxq_gemv_config fills these from the caller's request.
 struct GemvConfig {
     int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
     int rows_grid = 0;  // 0: min(tiles, resident); 1: equal tiles per workgroup; 2: one workgroup per tile
     // Path: 0 = by batch (FMA rows at batch 1, matrix-mode rows at 2 .. 4,
     // matrix unit from 5), 1 = matrix unit, 2 = FMA rows, 4 = matrix-mode rows
-    // (batch <= 4; mfma_ks = k split across waves, mfma_r = four-row groups).
+    // (batch <= 4).
     int path = 0;
-    // Matrix-unit settings: rows per wave (x16), k split, waves per workgroup,
-    // workgroups per CU; mfma_ks == 0 = chosen from the shape.
+    int mm_r = 0, mm_s = 0;
     int mfma_r = 0, mfma_ks = 0, mfma_nw = 0, mfma_occ = 0;
 };
 
@@ -76,7 +79,6 @@ struct GemmArgs {
     int64_t m, n, k;
 };
 
-GemvConfig choose_gemv_config(int fmt, int64_t n, int64_t k, int64_t batch);
 bool launch_gemv(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st);
 bool launch_moe(const MoeArgs& a, hipStream_t st);
 

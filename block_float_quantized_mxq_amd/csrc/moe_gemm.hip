@@ -20,9 +20,6 @@
 // value is computed by the same arithmetic wherever its pair sits in a block,
 // so results are identical run to run.  A pair whose id is outside [0, E) gets
 // a NaN output row.
-#include <cstdio>
-#include <cstdlib>
-
 #include "block_operand.hpp"
 #include "gemv_mfma.hpp"
 #include "kernels.hpp"
@@ -276,12 +273,6 @@ static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     for (const auto& c : kCand) {
         const int64_t cap = 4LL * c[0] * c[1];
         if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = c[0]; best_mb = c[1]; best_cap = cap; }
-    }
-    if (const char* env = std::getenv("MXQ_MOE_GEMM_TILE")) {  // "ks,mb": tuning override
-        int ks = 0, mb = 0;
-        if (std::sscanf(env, "%d,%d", &ks, &mb) == 2 && 4LL * ks * mb >= nblk)
-            for (const auto& c : kCand)
-                if (c[0] == ks && c[1] == mb) { best_ks = ks; best_mb = mb; }
     }
     if (best_ks == 0) return false;
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff, gperm,

@@ -14,9 +14,6 @@
 // scratch memory.  A position whose id is outside [0, E) gets NaN outputs.
 #pragma once
 
-#include <cstdio>
-#include <cstdlib>
-
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
@@ -182,8 +179,7 @@ static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
 // MI355X measurements: rows of >= 64 chunks take 16 lanes and 2 rows per
 // lane up to four tokens and 8 lanes with one row per lane beyond; shorter
 // rows take 8 lanes up to two tokens and 4 lanes beyond (more rows per
-// workgroup for the same activations).  MXQ_MOE_ROWS="g,s,r" overrides the
-// choice (used only to compare variants when tuning).
+// workgroup for the same activations).
 template <int FMT, int CB>
 static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
@@ -195,7 +191,6 @@ static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
         g = 8;
         r = 1;
     }
-    if (const char* env = std::getenv("MXQ_MOE_ROWS")) std::sscanf(env, "%d,%d,%d", &g, &sp, &r);
 #define MXQ_MOE_CASE(G_, S_, R_)                        \
     if (g == G_ && sp == S_ && r == R_) {              \
         launch_moe_inst<FMT, CB, G_, S_, R_>(a, st);   \

@@ -101,6 +101,34 @@ mxq_status_t mxq_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, cons
                       const uint16_t *x, float *y, int64_t n, int64_t k, int64_t batch, void *stream);
 
 /*
+ * Kernel configuration of the dense GEMV, for tests and tuning: the same
+ * product as mxq_gemv with the kernel and its tile chosen by the caller
+ * instead of from the shape.  Every field 0 means "chosen from the shape".
+ *   path    0 by batch (FMA rows at batch 1, matrix-mode rows at 2..4, the
+ *           matrix-unit GEMV from 5), 1 matrix-unit GEMV, 2 FMA rows,
+ *           4 matrix-mode rows (batch <= 4)
+ *   rows_g, rows_s, rows_r   FMA rows: lanes per row, k split, rows per lane
+ *   mm_r, mm_s               matrix-mode rows: four-row groups per lane, k
+ *                            split across waves
+ *   mfma_r, mfma_ks, mfma_nw matrix-unit GEMV: row blocks per wave, k split,
+ *                            waves per workgroup
+ *   per_cu                   workgroups per compute unit
+ * A configuration that is not compiled returns MXQ_E_UNSUPPORTED and runs
+ * nothing; config NULL is MXQ_E_NULLPTR.  Arguments as for mxq_gemv.
+ */
+typedef struct {
+    int32_t path;
+    int32_t rows_g, rows_s, rows_r;
+    int32_t mm_r, mm_s;
+    int32_t mfma_r, mfma_ks, mfma_nw;
+    int32_t per_cu;
+} mxq_gemv_config_t;
+
+mxq_status_t mxq_gemv_config(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                             const uint16_t *x, float *y, int64_t n, int64_t k, int64_t batch,
+                             const mxq_gemv_config_t *config, void *stream);
+
+/*
  * Expert-indexed MoE GEMV: every routed (token, slot) pair multiplies its
  * activation vector by the weight of the expert it is routed to, and only the
  * routed experts' weights are read, each expert once per call however many
@@ -307,7 +335,7 @@ mxq_status_t mxq_requant_fp8(const uint8_t *codes_in, const float *tile_scales, 
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 5 (4 plus mxq_requant_fp8). */
+/* ABI version of this header: 6 (5 plus mxq_gemv_config). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["mxq_gemv", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
+        ["mxq_gemv", "mxq_gemv_config", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
          "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_status_string",
          "mxq_abi_version"])
 
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 5
+    assert lib.mxq_abi_version() == 6
 
 
 def test_status_strings():
@@ -181,6 +181,22 @@ def test_unsupported_sizes():
     assert quant(rows=1 << 20, k=(1 << 16) + 32) == UNSUPPORTED and quant(rows=1 << 31) == UNSUPPORTED
 
 
+def gemv_cfg(config, **kw):
+    import ctypes
+    args = dict(fmt=1, codes=A, scales=A, g=None, x=A, y=A, n=8, k=64, batch=1)
+    args.update(kw)
+    c = ctypes.byref(mxq.GemvConfig(**config)) if config is not None else None
+    return mxq.lib().mxq_gemv_config(args["fmt"], args["codes"], args["scales"], args["g"], args["x"], args["y"],
+                                     args["n"], args["k"], args["batch"], c, None)
+
+
+def test_gemv_config_argument_errors():
+    assert gemv_cfg(None) == NULLPTR
+    assert gemv_cfg(dict(), fmt=0) == FORMAT and gemv_cfg(dict(), n=0) == SHAPE
+    assert gemv_cfg(dict(path=3)) == UNSUPPORTED and gemv_cfg(dict(path=-1)) == UNSUPPORTED
+    assert gemv_cfg(dict(path=4), batch=5) == UNSUPPORTED and gemv_cfg(dict(rows_g=-1)) == UNSUPPORTED
+
+
 def requant(ci=A, ts=A, co=A, sc=A, n=4, k=256, bn=128, bk=128):
     return mxq.lib().mxq_requant_fp8(ci, ts, co, sc, n, k, bn, bk, None)
 
@@ -211,6 +227,7 @@ def test_device_error_without_gpu():
     assert block_na() == DEVICE and block_na(T=8, topk=16, dff=2048, E=16) == DEVICE
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
     assert requant() == DEVICE and requant(n=1 << 20, k=1 << 16, bn=1, bk=32) == DEVICE
+    assert gemv_cfg(dict()) == DEVICE and gemv_cfg(dict(path=4, mm_r=4, mm_s=2), batch=4) == DEVICE
 
 
 def test_binding_rejects_cpu_tensors():

@@ -13,8 +13,9 @@ weight itself wherever the row's other weights are finite, and NaN where one of
 them is infinite or NaN (inf * 0).  The only difference allowed is the sign of
 a zero: a sum of -0 and +0 terms is +0.
 
-The kernels checked: the FMA GEMV at batches 1, 2 and 4, the matrix-unit GEMV
-at batch 8 (and forced at batch 1), the expert-indexed MoE GEMV (one pair per
+The kernels checked: the FMA GEMV at batch 1 (and forced at batch 4), the
+matrix-mode GEMV at batches 2 and 4 (and forced at batch 1), the matrix-unit
+GEMV at batch 8 (and forced at batch 1), the expert-indexed MoE GEMV (one pair per
 round at one token, two from two tokens up), the prefill GEMM on its tile path
 (m > 32) and its small-m path, and the expert-batched MoE GEMM.  The MoE decode
 block's down projection runs the FMA GEMV's decode (the same streaming engine).
@@ -102,7 +103,7 @@ def test_dequant(tile):
 
 @pytest.mark.parametrize("batch", [1, 2, 4, 8])
 def test_gemv(tile, batch):
-    """Batches 1, 2, 4: FMA path; batch 8: matrix-unit path."""
+    """Batch 1: FMA rows; batches 2, 4: matrix-mode rows; batch 8: matrix-unit GEMV."""
     fmt = tile["fmt"]
     for b0 in range(0, 8, batch):
         cols = J[b0:b0 + batch]
@@ -111,13 +112,19 @@ def test_gemv(tile, batch):
         check(y, tile["y_ref"][b0:b0 + batch], tile["t"], f"gemv batch {batch} columns {list(cols)}")
 
 
-def test_gemv_matrix_unit_batch1(tile, monkeypatch):
-    monkeypatch.setenv("MXQ_GEMV_MFMA", "1")
+@pytest.mark.parametrize("path", [1, 2, 4])
+def test_gemv_forced_paths(tile, path):
+    """Batch 1 through the matrix-unit GEMV (1), batch 4 through the FMA rows (2), and
+    batch 1 through the matrix-mode rows (4): the paths the default choice does not take
+    at those batches."""
     fmt = tile["fmt"]
-    for b in range(3):
-        say("decode paths: matrix-unit gemv batch 1", NAMES[fmt], J[b])
-        y = host(mxq.gemv(fmt, tile["codes"], tile["scales"], dev_bf16(one_hot([J[b]])), tile["gdev"]))
-        check(y, tile["y_ref"][b:b + 1], tile["t"], f"matrix-unit gemv column {J[b]}")
+    batch = 4 if path == 2 else 1
+    for b0 in range(0, 8, batch):
+        cols = J[b0:b0 + batch]
+        say("decode paths: gemv path", path, NAMES[fmt], list(cols))
+        y = host(mxq.gemv(fmt, tile["codes"], tile["scales"], dev_bf16(one_hot(cols)), tile["gdev"],
+                          config=dict(path=path)))
+        check(y, tile["y_ref"][b0:b0 + batch], tile["t"], f"gemv path {path} columns {list(cols)}")
 
 
 def _bank(tile):

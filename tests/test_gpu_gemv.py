@@ -14,24 +14,24 @@ pytestmark = pytest.mark.gpu
 FMT_NAMES = {1: "mxfp4", 2: "mxfp8", 3: "nvfp4"}
 
 
-def run(case, x=None):
+def run(case, x=None, config=None):
     x = case["x"] if x is None else x
     return host(mxq.gemv(case["fmt"], dev_u8(case["codes"]), dev_u8(case["scales"]), dev_bf16(x),
-                         dev_f32(case["g"])))
+                         dev_f32(case["g"]), config=config))
 
 
-def check_all(case, what):
+def check_all(case, what, config=None):
     say(what)
-    y = run(case)
+    y = run(case, config=config)
     y_ref, a_ref = oracle.gemv(case["fmt"], case["codes"], case["scales"], case["g"], case["x"], case["n"], case["k"])
     assert_within(y, y_ref, a_ref, what)
     return y
 
 
-def check_rows(case, rows, what):
+def check_rows(case, rows, what, config=None):
     """Full-size launch; the oracle recomputes the sampled rows one by one."""
     say(what)
-    y = run(case)
+    y = run(case, config=config)
     y_ref, a_ref = oracle.gemv(case["fmt"], case["codes"][rows], case["scales"][rows], case["g"], case["x"],
                                rows.size, case["k"])
     assert_within(y[:, rows], y_ref, a_ref, what)
@@ -197,37 +197,39 @@ def test_rejects_bad_arguments_on_gpu():
         mxq.gemv(3, codes, torch.zeros(8, 2, dtype=torch.uint8, device="cuda:0"), x[:1])  # NVFP4 without g
 
 
-MFMA_SETTINGS = ["1,1,1,4,0", "1,2,1,4,0", "1,4,1,4,0", "1,1,2,4,0", "1,1,4,4,0", "1,2,4,4,0", "1,4,4,4,0", "1,2,8,8,0"]
+# Matrix-unit GEMV settings (row blocks per wave, k split, waves per workgroup).
+MFMA_SETTINGS = [(1, 1, 4), (2, 1, 4), (4, 1, 4), (1, 2, 4), (1, 4, 4), (2, 4, 4), (4, 4, 4), (2, 8, 8)]
 
 
 @pytest.mark.parametrize("setting", MFMA_SETTINGS)
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("n,k", [(1000, 5120), (77, 25600), (129, 768), (300, 96), (64, 4096)])
-def test_matrix_unit_settings_all_outputs(setting, fmt, n, k, monkeypatch):
+def test_matrix_unit_settings_all_outputs(setting, fmt, n, k):
     """Every compiled (rows per wave, k split, waves) setting of the matrix-unit
     GEMV, forced for batches 1, 3 and 8, every output checked (ragged row
     blocks, k ranges that end inside a pass, empty k ranges)."""
-    monkeypatch.setenv("MXQ_GEMV_MFMA", setting)
+    r, ks, nw = setting
+    config = dict(path=1, mfma_r=r, mfma_ks=ks, mfma_nw=nw)
     sc, ss, sx, _, _ = synth.streams(7 * n + k + fmt)
     codes, scales, g = synth.weights(fmt, sc, ss, n, k)
     for batch in (1, 3, 8):
         x = synth.bf16_normal(sx, (batch, k))
         check_all(dict(fmt=fmt, codes=codes, scales=scales, g=g, x=x, n=n, k=k),
-                  f"matrix unit {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}")
+                  f"matrix unit {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}", config)
 
 
-# Matrix-mode rows (4 = path, then four-row groups per lane, k split across waves).
-MM_SETTINGS = ["4,4,1,0,0", "4,4,2,0,0", "4,4,4,0,0", "4,2,2,0,0", "4,2,4,0,0"]
+# Matrix-mode rows (four-row groups per lane, k split across waves).
+MM_SETTINGS = [(4, 1), (4, 2), (4, 4), (2, 2), (2, 4)]
 
 
 @pytest.mark.parametrize("setting", MM_SETTINGS)
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("n,k", [(1000, 5120), (77, 25600), (129, 768), (300, 96), (5, 4112)])
-def test_matrix_mode_settings_all_outputs(setting, fmt, n, k, monkeypatch):
+def test_matrix_mode_settings_all_outputs(setting, fmt, n, k):
     """Every compiled matrix-mode setting (16 x 16 x 32 MFMA on the FMA-mode
     loads), forced for batches 1 .. 4, every output checked: ragged row groups,
     rows shorter than one pass, NVFP4 rows of 8-byte chunks (k = 4112)."""
-    monkeypatch.setenv("MXQ_GEMV_MFMA", setting)
+    config = dict(path=4, mm_r=setting[0], mm_s=setting[1])
     if k % (16 if fmt == 3 else 32):
         k += 16  # MX formats: whole 32-element blocks
     sc, ss, sx, _, _ = synth.streams(11 * n + k + fmt)
@@ -235,14 +237,25 @@ def test_matrix_mode_settings_all_outputs(setting, fmt, n, k, monkeypatch):
     for batch in (1, 2, 3, 4):
         x = synth.bf16_normal(sx, (batch, k))
         check_all(dict(fmt=fmt, codes=codes, scales=scales, g=g, x=x, n=n, k=k),
-                  f"matrix mode {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}")
+                  f"matrix mode {setting} {FMT_NAMES[fmt]} n={n} k={k} B={batch}", config)
 
 
-def test_matrix_unit_and_fma_paths_agree_at_batch_one(monkeypatch):
-    """The two GEMV paths on the same full-size gate/up input: each within the
-    acceptance bound of the oracle on sampled rows."""
-    case = synth.dense_layer("gate_up", 1, seed=3)
-    rows = sample_rows(case["n"], 256, seed=3)
-    for path in ("1", "2"):
-        monkeypatch.setenv("MXQ_GEMV_MFMA", path)
-        check_rows(case, rows, f"gate/up B=1 path {path}")
+def test_every_path_at_full_size():
+    """Each GEMV path (matrix unit, FMA rows, matrix-mode rows) forced on the same
+    full-size gate/up input at batches 1 and 4: each within the acceptance bound
+    of the oracle on sampled rows."""
+    for batch in (1, 4):
+        case = synth.dense_layer("gate_up", batch, seed=3)
+        rows = sample_rows(case["n"], 256, seed=3)
+        for path in (1, 2, 4):
+            check_rows(case, rows, f"gate/up B={batch} path {path}", dict(path=path))
+
+
+def test_config_entry_point_rejects_uncompiled_settings():
+    case = synth.single_gemv(0)
+    with pytest.raises(mxq.MxqError) as e:
+        run(case, config=dict(path=2, rows_g=16, rows_s=3, rows_r=2))  # k split 3 is not compiled
+    assert e.value.status == 5
+    with pytest.raises(mxq.MxqError) as e:
+        run(case, config=dict(path=7))
+    assert e.value.status == 5
