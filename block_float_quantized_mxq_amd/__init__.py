@@ -41,7 +41,7 @@ _lib = None
 class GemvConfig(ctypes.Structure):
     """mxq_gemv_config_t: the dense GEMV's kernel and tile, for tests and tuning (0 = chosen from the shape)."""
     _fields_ = [(f, ctypes.c_int32) for f in ("path", "rows_g", "rows_s", "rows_r", "mm_r", "mm_s", "mfma_r",
-                                               "mfma_ks", "mfma_nw", "per_cu")]
+                                               "mfma_ks", "mfma_nw", "per_cu", "grid")]
 
 
 def lib() -> ctypes.CDLL:
@@ -63,8 +63,9 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_requant_fp8.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
+        L.mxq_stream_read.argtypes = [P, I64, I, P, I64, P]
         for f in (L.mxq_gemv, L.mxq_gemv_config, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
-                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8):
+                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8, L.mxq_stream_read):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -372,6 +373,20 @@ def dequant(fmt, codes, scales, global_scale=None, out=None, stream=None):
     _check(lib().mxq_dequant(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(out), rows, k,
                              _stream(stream)), "mxq_dequant")
     return out
+
+
+def stream_read(data, sink, nbytes=None, layout=0, stream=None):
+    """Streaming read of the first nbytes (default: all) of a contiguous device tensor (the
+    achievable-bandwidth reference; layout 0 interleaved, 1 contiguous range per workgroup);
+    sink: int32 device tensor of at least 8 words per CU."""
+    if not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous device tensor")
+    sink = _dev(sink, torch.int32, "sink")
+    nb = data.numel() * data.element_size() if nbytes is None else int(nbytes)
+    if nb > data.numel() * data.element_size():
+        raise ValueError("nbytes exceeds the tensor")
+    _check(lib().mxq_stream_read(_ptr(data), nb, int(layout), _ptr(sink), sink.numel(), _stream(stream)),
+           "mxq_stream_read")
 
 
 def weight_bytes(fmt, n, k):

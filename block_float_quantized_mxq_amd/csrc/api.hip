@@ -92,7 +92,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 6; }
+MXQ_API int mxq_abi_version(void) { return 7; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -123,6 +123,7 @@ MXQ_API mxq_status_t mxq_gemv_config(int fmt, const uint8_t* codes, const uint8_
     const int32_t fields[] = {c.rows_g, c.rows_s, c.rows_r, c.mm_r, c.mm_s, c.mfma_r, c.mfma_ks, c.mfma_nw, c.per_cu};
     for (int32_t f : fields)
         if (f < 0 || f > 64) return MXQ_E_UNSUPPORTED;
+    if (c.grid < 0 || c.grid > 3) return MXQ_E_UNSUPPORTED;
     if (c.path != 0 && c.path != 1 && c.path != 2 && c.path != 4) return MXQ_E_UNSUPPORTED;
     if (c.path == 4 && batch > 4) return MXQ_E_UNSUPPORTED;
     int cus = 0;
@@ -133,6 +134,7 @@ MXQ_API mxq_status_t mxq_gemv_config(int fmt, const uint8_t* codes, const uint8_
     cfg.rows_s = c.rows_s;
     cfg.rows_r = c.rows_r;
     cfg.rows_occ = c.per_cu;
+    cfg.rows_grid = c.grid;
     cfg.mm_r = c.mm_r;
     cfg.mm_s = c.mm_s;
     cfg.mfma_r = c.mfma_r;
@@ -255,6 +257,20 @@ MXQ_API mxq_status_t mxq_requant_fp8(const uint8_t* codes_in, const float* tile_
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     const mxq::RequantArgs a{codes_in, tile_scales, codes, scales, n, k, block_n, block_k};
     return launched(mxq::launch_requant_fp8(a, as_stream(stream)));
+}
+
+MXQ_API mxq_status_t mxq_stream_read(const void* data, int64_t bytes, int layout, uint32_t* sink,
+                                     int64_t sink_words, void* stream) {
+    if (!data || !sink) return MXQ_E_NULLPTR;
+    if (bytes <= 0 || bytes % 16 != 0 || sink_words <= 0) return MXQ_E_SHAPE;
+    if (layout != 0 && layout != 1) return MXQ_E_FORMAT;
+    if (!aligned(data, 16) || !aligned(sink, 4)) return MXQ_E_ALIGN;
+    int cus = 0;
+    mxq_status_t st;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    const int64_t want = (int64_t)cus * mxq::kStreamReadPerCu;
+    if (sink_words < want) return MXQ_E_UNSUPPORTED;
+    return launched(mxq::launch_stream_read(data, bytes, sink, want, layout, as_stream(stream)));
 }
 
 MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,

@@ -34,7 +34,8 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ gscale,
                                                              const uint16_t* __restrict__ x, float* __restrict__ y,
-                                                             int64_t n, int64_t k, int batch, int64_t ntiles) {
+                                                             int64_t n, int64_t k, int batch, int64_t ntiles,
+                                                             int contiguous) {
     using T = RowTile<G, S, R>;
     using E = RowEngine<FMT, CB, B, G, S, R, XL, false, MM>;
     __shared__ float red[E::RED_FLOATS];
@@ -47,9 +48,21 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(const uint8_t* __re
         ys[b] = b < batch ? y + (int64_t)b * n : nullptr;
     }
     const E eng(codes, scales, n, k);
-    const int64_t tile = blockIdx.x;  // < ntiles: the grid never exceeds the tile count
-    const int64_t count = (ntiles - tile + gridDim.x - 1) / gridDim.x;
-    typename E::Cursor cur = eng.cursor(tile * T::ROWS, (int64_t)gridDim.x * T::ROWS, count, xs[0]);
+    // tiles w, w + grid, w + 2 grid, ... (interleaved) or one contiguous range of
+    // tiles per workgroup; the grid never exceeds the tile count
+    const int64_t w = blockIdx.x, grid = gridDim.x;
+    int64_t first, step, count;
+    if (contiguous) {
+        const int64_t per = ntiles / grid, rem = ntiles % grid;
+        first = w * per + (w < rem ? w : rem);
+        count = per + (w < rem ? 1 : 0);
+        step = 1;
+    } else {
+        first = w;
+        count = (ntiles - w + grid - 1) / grid;
+        step = grid;
+    }
+    typename E::Cursor cur = eng.cursor(first * T::ROWS, step * T::ROWS, count, xs[0]);
     PassRing<typename E::Pass, kGemvAhead + 1> ring;
     eng.template prime<kGemvAhead>(cur, ring);
     const float gmul = (FMT == kNVFP4) ? gscale[0] : 1.0f;
@@ -96,8 +109,9 @@ static void launch_rows_inst(const GemvArgs& a, int64_t per_cu, int grid_mode, h
     } else if (grid_mode == 2) {
         blocks = ntiles;
     }
+    const int contiguous = grid_mode == 3 ? 1 : 0;
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), lds, st, a.codes, a.scales, a.gscale, a.x, a.y,
-                       a.n, a.k, (int)a.batch, ntiles);
+                       a.n, a.k, (int)a.batch, ntiles, contiguous);
 }
 
 // Row-tile settings (lanes per row g, k split s, rows per lane r, workgroups

@@ -30,7 +30,9 @@ struct GemvArgs {
 // CU (mfma_occ).  mxq_gemv_config fills these from the caller's request.
 struct GemvConfig {
     int rows_g = 0, rows_s = 0, rows_r = 0, rows_occ = 0;
-    int rows_grid = 0;  // 0: min(tiles, resident); 1: equal tiles per workgroup; 2: one workgroup per tile
+    // 0: min(tiles, resident), tiles interleaved; 1: equal tiles per workgroup; 2: one workgroup per
+    // tile; 3: min(tiles, resident), one contiguous range of tiles per workgroup
+    int rows_grid = 0;
     // Path: 0 = by batch (FMA rows at batch 1, matrix-mode rows at 2 .. 4,
     // matrix unit from 5), 1 = matrix unit, 2 = FMA rows, 4 = matrix-mode rows
     // (batch <= 4).
@@ -158,6 +160,14 @@ struct RequantArgs {
     int64_t n, k, bn, bk;
 };
 bool launch_requant_fp8(const RequantArgs& a, hipStream_t st);
+
+// Streaming read of `bytes` (a multiple of 16) on `workgroups` workgroups,
+// lanes interleaved over the range or one contiguous range per workgroup;
+// sink[w] receives workgroup w's fold of the words it read.
+bool launch_stream_read(const void* p, int64_t bytes, uint32_t* sink, int64_t workgroups, int contiguous,
+                        hipStream_t st);
+// Workgroups of the streaming read: as many as are resident on the device.
+constexpr int kStreamReadPerCu = 8;
 bool launch_moe_route(const RouteArgs& a, hipStream_t st);
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st);
 bool launch_moe_down(const MoeBlockArgs& a, hipStream_t st);

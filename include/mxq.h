@@ -113,6 +113,10 @@ mxq_status_t mxq_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, cons
  *   mfma_r, mfma_ks, mfma_nw matrix-unit GEMV: row blocks per wave, k split,
  *                            waves per workgroup
  *   per_cu                   workgroups per compute unit
+ *   grid                     FMA and matrix-mode rows: 0 as many workgroups as are resident,
+ *                            tiles interleaved; 1 equal tile counts; 2 one
+ *                            workgroup per tile; 3 as 0 with one contiguous
+ *                            range of tiles per workgroup
  * A configuration that is not compiled returns MXQ_E_UNSUPPORTED and runs
  * nothing; config NULL is MXQ_E_NULLPTR.  Arguments as for mxq_gemv.
  */
@@ -122,6 +126,7 @@ typedef struct {
     int32_t mm_r, mm_s;
     int32_t mfma_r, mfma_ks, mfma_nw;
     int32_t per_cu;
+    int32_t grid;
 } mxq_gemv_config_t;
 
 mxq_status_t mxq_gemv_config(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
@@ -332,10 +337,26 @@ mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale,
 mxq_status_t mxq_requant_fp8(const uint8_t *codes_in, const float *tile_scales, uint8_t *codes, uint8_t *scales,
                              int64_t n, int64_t k, int64_t block_n, int64_t block_k, void *stream);
 
+/*
+ * Measurement reference: a plain streaming read of `bytes` bytes at `data`
+ * (16-byte loads with the nontemporal hint, as the GEMV reads its codes, on 8
+ * workgroups per compute unit), the achievable bandwidth the GEMV kernels are
+ * compared with ("The memory wall" section of the post, slide 15 of the talk:
+ * decode time is the time to stream the weights).  layout 0: lanes
+ * interleaved over the range; 1: one contiguous range per workgroup (other
+ * values: MXQ_E_FORMAT).  The words read are XOR-folded into
+ * sink[0 .. workgroups), so the loads cannot be dropped.
+ *   data        16-byte aligned;  bytes a positive multiple of 16
+ *   sink        uint32 [sink_words]; sink_words >= 8 * compute units (256 CUs:
+ *               2048), else MXQ_E_UNSUPPORTED
+ */
+mxq_status_t mxq_stream_read(const void *data, int64_t bytes, int layout, uint32_t *sink, int64_t sink_words,
+                             void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 6 (5 plus mxq_gemv_config). */
+/* ABI version of this header: 7 (6 plus mxq_stream_read). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["mxq_gemv", "mxq_gemv_config", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
-         "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_status_string",
+         "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_stream_read",
+         "mxq_status_string",
          "mxq_abi_version"])
 
 
@@ -36,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 6
+    assert lib.mxq_abi_version() == 7
 
 
 def test_status_strings():
@@ -195,6 +196,14 @@ def test_gemv_config_argument_errors():
     assert gemv_cfg(dict(), fmt=0) == FORMAT and gemv_cfg(dict(), n=0) == SHAPE
     assert gemv_cfg(dict(path=3)) == UNSUPPORTED and gemv_cfg(dict(path=-1)) == UNSUPPORTED
     assert gemv_cfg(dict(path=4), batch=5) == UNSUPPORTED and gemv_cfg(dict(rows_g=-1)) == UNSUPPORTED
+
+
+def test_stream_read_argument_errors():
+    sr = mxq.lib().mxq_stream_read
+    assert sr(None, 16, 0, A, 4096, None) == NULLPTR and sr(A, 16, 0, None, 4096, None) == NULLPTR
+    assert sr(A, 0, 0, A, 4096, None) == SHAPE and sr(A, 24, 0, A, 4096, None) == SHAPE
+    assert sr(A, 16, 0, A, 0, None) == SHAPE and sr(A, 16, 2, A, 4096, None) == FORMAT
+    assert sr(A + 8, 16, 1, A, 4096, None) == ALIGN and sr(A, 16, 1, A + 2, 4096, None) == ALIGN
 
 
 def requant(ci=A, ts=A, co=A, sc=A, n=4, k=256, bn=128, bk=128):
