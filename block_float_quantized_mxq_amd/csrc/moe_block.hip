@@ -18,7 +18,7 @@
 //    routing weights in a fixed order -- no atomics, bit-reproducible.
 //  * a token with an expert id outside [0, E) gets NaN outputs.
 //
-// Routing: one workgroup per token.  Selection compares the fp32 logits
+// Routing: one wave per token.  Selection compares the fp32 logits
 // themselves (larger first, equal logits: lower index first), so it does not
 // depend on how the softmax is rounded; the weights are the softmax
 // probabilities of the selected experts, optionally renormalised over them.
@@ -32,118 +32,128 @@ namespace mxq {
 
 // ---- routing ---------------------------------------------------------------------
 
-__device__ __forceinline__ void take_better(float& v, int& i, float ov, int oi) {
-    if (ov > v || (ov == v && oi < i)) {
-        v = ov;
-        i = oi;
-    }
-}
-
+// Wave-uniform integer maximum and float sum: four DPP steps inside each row
+// of 16 lanes, then the four row results are read into scalar registers and
+// combined in a fixed order (row 0, 1, 2, 3), so every lane has the same bits.
 template <int CTRL>
 __device__ __forceinline__ int dpp_i32(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
-// Largest (value, index) pair of the wave, equal values: lower index; every
-// lane ends with it.  Inside each row of 16 lanes the partners come from DPP
-// (swap neighbours, swap pairs, mirror halves, mirror the row: each step
-// pairs every lane with one that holds the other half of its group), across
-// rows from two shuffles.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-    take_better(v, i, dpp_f32<kDppQuadXor1>(v), dpp_i32<kDppQuadXor1>(i));
-    take_better(v, i, dpp_f32<kDppQuadXor2>(v), dpp_i32<kDppQuadXor2>(i));
-    take_better(v, i, dpp_f32<kDppRowHalfMirror>(v), dpp_i32<kDppRowHalfMirror>(i));
-    take_better(v, i, dpp_f32<kDppRowMirror>(v), dpp_i32<kDppRowMirror>(i));
-    take_better(v, i, __shfl_xor(v, 16, 64), __shfl_xor(i, 16, 64));
-    take_better(v, i, __shfl_xor(v, 32, 64), __shfl_xor(i, 32, 64));
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+__device__ __forceinline__ int wave_max_uniform(int v) {
+    v = imax(v, dpp_i32<kDppQuadXor1>(v));
+    v = imax(v, dpp_i32<kDppQuadXor2>(v));
+    v = imax(v, dpp_i32<kDppRowHalfMirror>(v));
+    v = imax(v, dpp_i32<kDppRowMirror>(v));
+    return imax(imax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                imax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// One workgroup per token.  The logits go to LDS; each expert's rank is the
-// number of logits that beat it (larger, or equal with a lower index), so the
-// selected experts are those of rank < topk and the rank is their output
-// slot -- the same order as picking the largest remaining logit topk times,
-// without topk serial rounds.  The softmax maximum and denominator are
-// workgroup reductions; the renormalising sum adds the selected
-// probabilities in slot order.
-constexpr int kRouteThreads = 256;
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+    v = group_sum<16>(v);
+    const auto rl = [](float x, int lane) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+    };
+    return ((rl(v, 0) + rl(v, 16)) + rl(v, 32)) + rl(v, 48);
+}
+
+// Order-preserving key of a float logit: signed-integer order of the keys is
+// the order of the values (-0 is taken as +0, so equal values have equal
+// keys); the inverse map is the same xor.
+__device__ __forceinline__ int logit_key(float f) {
+    int b = __builtin_bit_cast(int, f);
+    b = b == (int)0x80000000 ? 0 : b;
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key_logit(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+// One wave per token, everything in registers: lane l holds the keys of
+// experts l, l + 64, ... (NS of them, at most 16).  Slot s gets the expert of
+// rank s -- larger logit first, equal logits lower index first -- found in
+// round s: the wave maximum m of the keys not yet picked, then the lowest
+// index holding m, from one ballot per register slot (slot j holds experts
+// 64 j .. 64 j + 63, so the first non-empty ballot and its lowest lane give
+// the lowest index).  A picked expert's key becomes INT_MIN, below the key of
+// every logit, -inf included, so -inf logits stay candidates.  The softmax
+// maximum is round 0's winner; the probabilities are computed once, after the
+// rounds, by the lanes l < topk, and the renormalising sum is a wave sum of
+// them.  No LDS and no barrier.
 constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteSlots = kRouteMaxExperts / 64;
 
-__device__ __forceinline__ float wave_max(float v) {
-    int dummy = 0;
-    wave_argmax(v, dummy);
-    return v;
-}
-
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(const float* __restrict__ logits, int64_t experts,
-                                                                  int topk, int renorm, int32_t* __restrict__ ids,
-                                                                  float* __restrict__ weights) {
-    __shared__ __attribute__((aligned(16))) float lv[kRouteMaxExperts];
-    __shared__ float part[kRouteThreads / 64];
-    __shared__ float psel[16];
+template <int NS>
+__global__ __launch_bounds__(64) void moe_route_kernel(const float* __restrict__ logits, int64_t experts,
+                                                        int topk, int renorm, int32_t* __restrict__ ids,
+                                                        float* __restrict__ weights) {
+    constexpr int kPicked = (int)0x80000000;
     const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int l = threadIdx.x;
     const int E = (int)experts;
-    const float* l = logits + t * experts;
-
-    float mx = -__builtin_huge_valf();
-    for (int e = tid; e < E; e += kRouteThreads) {
-        const float v = l[e];
-        lv[e] = v;
-        mx = v > mx ? v : mx;
+    const float* lg = logits + t * experts;
+    float v[NS];
+    int key[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const bool in = l + 64 * j < E;
+        v[j] = in ? lg[l + 64 * j] : 0.0f;
+        key[j] = in ? logit_key(v[j]) : kPicked;
     }
-    for (int e = E + tid; e < ((E + 15) & ~15); e += kRouteThreads) lv[e] = -__builtin_huge_valf();  // pad to 16
-    mx = wave_max(mx);
-    if ((tid & 63) == 0) part[wave] = mx;
-    __syncthreads();
-    mx = part[0];
+    int top = kPicked, myk = kPicked, myi = -1;  // lane s ends with slot s's key and expert
+    for (int s = 0; s < topk; ++s) {
+        int m = key[0];
 #pragma unroll
-    for (int w = 1; w < kRouteThreads / 64; ++w) mx = part[w] > mx ? part[w] : mx;
-    __syncthreads();  // part is reused below
-
-    float den = 0.0f;
-    for (int e = tid; e < E; e += kRouteThreads) den += expf(lv[e] - mx);
-    den = group_sum<64>(den);
-    if ((tid & 63) == 0) part[wave] = den;
-    __syncthreads();
-    den = part[0];
+        for (int j = 1; j < NS; ++j) m = imax(m, key[j]);
+        m = wave_max_uniform(m);
+        int win = -1;
+        if (m != kPicked) {
 #pragma unroll
-    for (int w = 1; w < kRouteThreads / 64; ++w) den += part[w];
-
-    for (int e = tid; e < E; e += kRouteThreads) {
-        const float v = lv[e];
-        // 16 logits per step: four independent LDS reads in flight (the
-        // padding never counts: -inf beats nothing, and its index is past e)
-        int rank = 0;
-        for (int j0 = 0; j0 < E; j0 += 16) {
-            float4 o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = *reinterpret_cast<const float4*>(lv + j0 + 4 * q);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = j0 + 4 * q;
-                rank += (o[q].x > v || (o[q].x == v && j < e)) ? 1 : 0;
-                rank += (o[q].y > v || (o[q].y == v && j + 1 < e)) ? 1 : 0;
-                rank += (o[q].z > v || (o[q].z == v && j + 2 < e)) ? 1 : 0;
-                rank += (o[q].w > v || (o[q].w == v && j + 3 < e)) ? 1 : 0;
+            for (int j = 0; j < NS; ++j) {
+                if (win < 0) {
+                    const uint64_t hit = __ballot(key[j] == m);
+                    if (hit) {
+                        const int lane = __builtin_ctzll(hit);
+                        win = 64 * j + lane;
+                        if (l == lane) key[j] = kPicked;
+                    }
+                }
             }
         }
-        if (rank < topk) {
-            ids[t * topk + rank] = e;
-            psel[rank] = expf(v - mx) / den;
+        if (s == 0) top = m;
+        if (l == s) {
+            myk = m;
+            myi = win;
         }
     }
-    __syncthreads();
-    if (tid < topk) {
-        float sel = 0.0f;
-        for (int s = 0; s < topk; ++s) sel += psel[s];
-        weights[t * topk + tid] = renorm ? psel[tid] / sel : psel[tid];
+    const float mx = key_logit(top);
+    float den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        if (l + 64 * j < E) den += expf(v[j] - mx);
+    den = wave_sum_uniform(den);
+    const float p = l < topk ? expf(key_logit(myk) - mx) / den : 0.0f;
+    const float psum = renorm ? wave_sum_uniform(p) : 1.0f;
+    if (l < topk) {
+        ids[t * topk + l] = myi;
+        weights[t * topk + l] = renorm ? p / psum : p;
     }
+}
+
+template <int NS>
+static void launch_route_ns(const RouteArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(moe_route_kernel<NS>, dim3((unsigned)a.tokens), dim3(64), 0, st, a.logits, a.experts,
+                       (int)a.topk, a.renorm, a.ids, a.weights);
 }
 
 bool launch_moe_route(const RouteArgs& a, hipStream_t st) {
     if (a.experts > kRouteMaxExperts) return false;
-    hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)a.tokens), dim3(kRouteThreads), 0, st, a.logits, a.experts,
-                       (int)a.topk, a.renorm, a.ids, a.weights);
+    // logits per lane: the smallest compiled count that covers the experts
+    if (a.experts <= 64) launch_route_ns<1>(a, st);
+    else if (a.experts <= 128) launch_route_ns<2>(a, st);
+    else if (a.experts <= 256) launch_route_ns<4>(a, st);
+    else if (a.experts <= 512) launch_route_ns<8>(a, st);
+    else launch_route_ns<kRouteSlots>(a, st);
     return true;
 }
 
