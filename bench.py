@@ -340,7 +340,7 @@ def main():
             x = bf(synth.bf16_normal(sx, (T, 2048)))
             ids = torch.empty((T, 8), dtype=torch.int32, device=dev)
             wts = torch.empty((T, 8), dtype=torch.float32, device=dev)
-            h = torch.empty((T, 8, 1536), dtype=torch.float32, device=dev)
+            h = torch.empty(mxq.moe_block_workspace_elems(T, 8, 768), dtype=torch.float32, device=dev)
             y = torch.empty((T, 2048), dtype=torch.float32, device=dev)
             active = []
             for lg in logits:  # union of routed experts per set (for the byte count only)

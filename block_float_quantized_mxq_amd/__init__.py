@@ -200,11 +200,26 @@ def moe_route(logits, topk, renorm=False, ids=None, weights=None, stream=None):
     return ids, weights
 
 
+def moe_block_workspace_elems(tokens, topk, dff):
+    """float32 elements of the MoE block's workspace: tokens * topk * dff * 10 bytes."""
+    return tokens * topk * dff * 10 // 4
+
+
+def moe_block_workspace_views(h, tokens, topk, dff):
+    """(gate/up outputs float32 [tokens, topk, 2 dff], activations bfloat16 [tokens, topk, dff]) of a workspace."""
+    flat = h.reshape(-1)
+    n = tokens * topk * 2 * dff
+    act = flat[n:n + tokens * topk * dff // 2].view(torch.bfloat16)
+    return flat[:n].view(tokens, topk, 2 * dff), act.view(tokens, topk, dff)
+
+
 def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights, x, gu_global_scale=None,
               dn_global_scale=None, h=None, out=None, stream=None, noalloc=False):
     """MoE decode block -> float32 [tokens, hidden]: y[t] = sum_s w[t][s] * W_dn[e] . bf16(silu(gate) * up),
     with gate/up = W_gu[e] . x[t] (rows [0, dff) and [dff, 2 dff) of the gate/up bank).
-    h is the float32 [tokens, topk, 2 dff] workspace (allocated when None).  With noalloc the call goes to
+    h is the workspace (allocated when None): moe_block_workspace_elems(tokens, topk, dff) float32
+    elements holding the float32 gate/up outputs [tokens, topk, 2 dff], then the bfloat16 activations
+    [tokens, topk, dff] (see moe_block_workspace_views).  With noalloc the call goes to
     mxq_moe_block_noalloc, whose workspace is the library's static device array (h must be None; `out`
     is still allocated here when None)."""
     gu_codes = _dev(gu_codes, torch.uint8, "gu_codes")
@@ -230,11 +245,12 @@ def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights
         if h is not None:
             raise ValueError("noalloc takes no workspace")
     else:
+        need = moe_block_workspace_elems(tokens, topk, dff)
         if h is None:
-            h = torch.empty((tokens, topk, 2 * dff), dtype=torch.float32, device=gu_codes.device)
+            h = torch.empty(need, dtype=torch.float32, device=gu_codes.device)
         h = _dev(h, torch.float32, "h")
-        if h.numel() < tokens * topk * 2 * dff:
-            raise ValueError("h must hold tokens * topk * 2 * dff elements")
+        if h.numel() < need:
+            raise ValueError(f"h must hold moe_block_workspace_elems(tokens, topk, dff) = {need} elements")
     if out is None:
         out = torch.empty((tokens, hidden), dtype=torch.float32, device=gu_codes.device)
     out = _dev(out, torch.float32, "out")

@@ -92,7 +92,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 7; }
+MXQ_API int mxq_abi_version(void) { return 8; }
 
 MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -321,18 +321,21 @@ mxq_status_t check_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu
     return MXQ_OK;
 }
 
-// The block's two kernels on validated arguments, with the gate/up outputs in h.
+// The block's two kernels on validated arguments, with the workspace at h.
 mxq_status_t run_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
                            const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
                            const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h, float* y,
                            int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk, int cus,
                            void* stream) {
     mxq_status_t st;
-    const mxq::MoeArgs gu{fmt, gu_codes, gu_scales, gu_gscale, expert_ids, x, 0, h, num_experts, 2 * dff, hidden,
-                          tokens, topk, cus};
+    // workspace: gate/up outputs, then the bf16 activations
+    uint16_t* act = reinterpret_cast<uint16_t*>(h + tokens * topk * 2 * dff);
+    mxq::MoeArgs gu{fmt, gu_codes, gu_scales, gu_gscale, expert_ids, x, 0, h, num_experts, 2 * dff, hidden,
+                    tokens, topk, cus};
+    gu.act = act;
     if ((st = launched(mxq::launch_moe(gu, as_stream(stream)))) != MXQ_OK) return st;
-    const mxq::MoeBlockArgs dn{fmt, dn_codes, dn_scales, dn_gscale, expert_ids, weights, h, y, num_experts, hidden, dff,
-                               tokens, topk};
+    const mxq::MoeBlockArgs dn{fmt, dn_codes, dn_scales, dn_gscale, expert_ids, weights, act, y, num_experts, hidden,
+                               dff, tokens, topk};
     return launched(mxq::launch_moe_down(dn, as_stream(stream)));
 }
 
@@ -360,7 +363,7 @@ MXQ_API mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t* gu_codes, con
     mxq_status_t st = check_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids,
                                       weights, x, nullptr, false, y, num_experts, hidden, dff, tokens, topk);
     if (st != MXQ_OK) return st;
-    if (tokens * topk * 2 * dff * (int64_t)sizeof(float) > mxq::kMoeBlockScratchBytes) return MXQ_E_UNSUPPORTED;
+    if (mxq::moe_block_workspace_bytes(tokens, topk, dff) > mxq::kMoeBlockScratchBytes) return MXQ_E_UNSUPPORTED;
     int cus = 0;
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     float* h = nullptr;

@@ -59,6 +59,9 @@ struct MoeArgs {
     float* y;
     int64_t experts, n, k, tokens, topk;
     int cus;  // compute units of the device
+    // non-null: the rows are a SwiGLU layer's gate rows then up rows (n even),
+    // and position q also gets bf16(silu(gate) * up) at act + q n/2
+    uint16_t* act = nullptr;
 };
 
 struct DequantArgs {
@@ -99,8 +102,8 @@ struct MoeBlockArgs {
     const float* dn_gscale;
     const int32_t* ids;
     const float* weights;
-    const float* h;  // gate/up outputs [tokens][topk][2 dff]
-    float* y;        // [tokens][hidden]
+    const uint16_t* act;  // bf16 SwiGLU activations [tokens][topk][dff]
+    float* y;             // [tokens][hidden]
     int64_t experts, hidden, dff, tokens, topk;
 };
 
@@ -108,11 +111,16 @@ struct MoeBlockArgs {
 // power of two, dff bf16 each).
 constexpr int64_t kMoeBlockMaxLds = 64 * 1024;
 
-// Allocation-free MoE block: the gate/up outputs h (fp32 [tokens][topk][2 dff])
-// live in a static device array of this many bytes, one per GPU.  Every call
-// the LDS budget admits fits (topk * dff <= 32768 and tokens <= 8 give at most
-// 2 MiB).
-constexpr int64_t kMoeBlockScratchBytes = int64_t(2) << 20;
+// The MoE block's workspace: the gate/up outputs (fp32 [tokens][topk][2 dff])
+// followed by the activations (bf16 [tokens][topk][dff]), 10 bytes per
+// (token, slot, expert-width column).
+constexpr int64_t moe_block_workspace_bytes(int64_t tokens, int64_t topk, int64_t dff) {
+    return tokens * topk * dff * 10;
+}
+// Allocation-free MoE block: the workspace lives in a static device array of
+// this many bytes, one per GPU.  Every call the LDS budget admits fits
+// (topk * dff <= 32768 and tokens <= 8 give at most 2.5 MiB).
+constexpr int64_t kMoeBlockScratchBytes = int64_t(5) << 19;
 // The array's device address on the current device (looked up once per device).
 hipError_t moe_block_scratch(float** ptr);
 

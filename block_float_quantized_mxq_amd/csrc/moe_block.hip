@@ -5,13 +5,14 @@
 //
 // The "affine MoE" row of the ROCm status table in the "Build from source"
 // manual runs single-token MoE decode as a fused two-kernel path, gate-up then
-// down; slide 13 of the talk lists that port.  Here the two kernels are the
-// expert-indexed gate/up GEMV (moe_impl.hpp, every routed expert read once)
-// and moe_down_kernel below:
+// down; slide 13 of the talk lists that port.  Here the two kernels are:
 //
-//  * grid (row tile of the hidden dimension, token); a workgroup first turns
-//    the token's gate/up outputs into its topk bf16 activation vectors
-//    a_s = bf16(silu(gate) * up) in LDS (rounded to nearest even once), then
+//  * the expert-indexed gate/up GEMV (moe_impl.hpp, every routed expert read
+//    once) in its paired-row mode: each lane holds gate row j and up row j of
+//    one expert, and the tile's end writes both outputs and the activation
+//    a_s[j] = bf16(silu(gate) * up) (fp32, rounded to nearest even once);
+//  * moe_down_kernel below, grid (row tile of the hidden dimension, token): a
+//    workgroup copies the token's topk activation vectors into LDS, then
 //    streams, for each of its output rows, the rows of the topk routed down
 //    matrices: group s of each row set reads expert ids[t][s] (the streaming
 //    engine's per-slot mode) and the groups' sums are combined with the
@@ -159,21 +160,13 @@ bool launch_moe_route(const RouteArgs& a, hipStream_t st) {
 
 // ---- down projection with SwiGLU input and weighted combine ---------------------------
 
-// a = bf16(silu(g) * u), computed in fp32 and rounded to nearest even once.
-__device__ __forceinline__ uint32_t swiglu_bf16x2(float g0, float u0, float g1, float u1) {
-    const float a0 = g0 / (1.0f + expf(-g0)) * u0;
-    const float a1 = g1 / (1.0f + expf(-g1)) * u1;
-    const bf16x2_t b = {(__bf16)a0, (__bf16)a1};
-    return __builtin_bit_cast(uint32_t, b);
-}
-
 template <int FMT, int CB, int G, int S, int R>
 __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ gscale,
                                                             const int32_t* __restrict__ ids,
                                                             const float* __restrict__ weights,
-                                                            const float* __restrict__ h, float* __restrict__ y,
+                                                            const uint16_t* __restrict__ act, float* __restrict__ y,
                                                             int64_t experts, int64_t hidden, int64_t dff, int topk) {
     using T = RowTile<G, S, R>;
     using E = RowEngine<FMT, CB, 1, G, S, R, true, true>;
@@ -207,40 +200,32 @@ __global__ __launch_bounds__(kThreads) void moe_down_kernel(const uint8_t* __res
     const int e = ids[t * topk + (sp < topk ? sp : 0)];
     const int64_t rowbytes = code_bytes_per_row(FMT, dff);
     const E eng(codes + (int64_t)e * hidden * rowbytes, scales + (int64_t)e * hidden * (dff / CS::BS), hidden, dff);
-    const uint16_t* xs[1] = {reinterpret_cast<const uint16_t*>(h)};
+    const uint16_t* xs[1] = {act};
     float* ys[1] = {y + t * hidden};
     RowCursor<R> cur = eng.cursor(row0, 0, 1, xs[0]);
     PassRing<RowPass<FMT, CB, R>, 2> ring;
     eng.template prime<1>(cur, ring);  // weights first: in flight while the activations are built
 
-    // activations of the token's slots, slot s at elements s*dff .. of the staged block
-    // (the h loads of U pieces per thread are issued together: one cache
-    // round trip per U pieces, not per piece)
-    constexpr int U = 3;
+    // the token's activations [topk][dff] (slot s at elements s*dff ..) into
+    // the staged block, 16 bytes a piece; the loads of U pieces per thread
+    // are issued together (one cache round trip per U pieces)
+    constexpr int U = 4;
     const int64_t pieces = (int64_t)topk * dff / 8;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(act + t * topk * dff);
     for (int64_t p0 = threadIdx.x; p0 < pieces; p0 += U * kThreads) {
-        float4 g[U][2], u[U][2];
+        u32x4_t v[U];
 #pragma unroll
         for (int w = 0; w < U; ++w) {
             const int64_t p = p0 + (int64_t)w * kThreads;
-            const int64_t pp = p < pieces ? p : p0;
-            const int64_t s = pp * 8 / dff, j = pp * 8 % dff;
-            const float* hg = h + (t * topk + s) * 2 * dff + j;
-            g[w][0] = *reinterpret_cast<const float4*>(hg);
-            g[w][1] = *reinterpret_cast<const float4*>(hg + 4);
-            u[w][0] = *reinterpret_cast<const float4*>(hg + dff);
-            u[w][1] = *reinterpret_cast<const float4*>(hg + dff + 4);
+            v[w] = src[p < pieces ? p : p0];
         }
 #pragma unroll
         for (int w = 0; w < U; ++w) {
             const int64_t p = p0 + (int64_t)w * kThreads;
             if (p < pieces) {
-                const float4 g0 = g[w][0], g1 = g[w][1], u0 = u[w][0], u1 = u[w][1];
-                const u32x4_t v = {swiglu_bf16x2(g0.x, u0.x, g0.y, u0.y), swiglu_bf16x2(g0.z, u0.z, g0.w, u0.w),
-                                   swiglu_bf16x2(g1.x, u1.x, g1.y, u1.y), swiglu_bf16x2(g1.z, u1.z, g1.w, u1.w)};
                 const int64_t c = p / CS::XQ;
                 const int q = (int)(p % CS::XQ);
-                reinterpret_cast<u32x4_t*>(xlds)[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v;
+                reinterpret_cast<u32x4_t*>(xlds)[c * CS::XQ + (q ^ x_swizzle<FMT, CB>(c))] = v[w];
             }
         }
     }
@@ -254,18 +239,18 @@ static void launch_down_inst(const MoeBlockArgs& a, hipStream_t st) {
     const int64_t tiles = (a.hidden + T::ROWS - 1) / T::ROWS;
     const size_t lds = (size_t)S * a.dff * 2;
     hipLaunchKernelGGL((moe_down_kernel<FMT, CB, G, S, R>), dim3((unsigned)tiles, (unsigned)a.tokens), dim3(kThreads),
-                       lds, st, a.dn_codes, a.dn_scales, a.dn_gscale, a.ids, a.weights, a.h, a.y, a.experts, a.hidden,
+                       lds, st, a.dn_codes, a.dn_scales, a.dn_gscale, a.ids, a.weights, a.act, a.y, a.experts, a.hidden,
                        a.dff, (int)a.topk);
 }
 
-// Rows per lane: a workgroup builds its token's activations once for all its
-// rows, so from two tokens 4 rows per lane (half the workgroups, half the
-// rebuilt activations) beat 2 (MI355X, 30B-A3B block: 4 tokens 33.0 -> 30.0 us,
-// 8 tokens 49.6 -> 45.0 us; one token 18.0 vs 18.6 us, so 2 there).
+// Two rows per lane at every token count: with the activations precomputed
+// by the gate/up kernel, 4 rows per lane (half the workgroups, each copying
+// its token's activations once) measure the same (MI355X, 30B-A3B block,
+// 2 and 4 tokens: 17.89 / 25.70 us with 4, 17.89 / 25.76 us with 2) and
+// one token is faster with 2 (14.74 vs 15.00 us).
 template <int FMT, int CB, int G, int S>
 static void launch_down_gs(const MoeBlockArgs& a, hipStream_t st) {
-    if (a.tokens >= 2) launch_down_inst<FMT, CB, G, S, 4>(a, st);
-    else launch_down_inst<FMT, CB, G, S, 2>(a, st);
+    launch_down_inst<FMT, CB, G, S, 2>(a, st);
 }
 
 // Slots rounded up to a power of two; 8 lanes per row while a slot's row has

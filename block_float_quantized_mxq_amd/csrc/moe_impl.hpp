@@ -62,11 +62,12 @@ __device__ __forceinline__ int next_position(uint64_t& m0, uint64_t& m1) {
 // One round: the B positions in q[0..B) (q < 0: unused slot) contracted with
 // the expert's row tile, with activations staged in LDS when XL.  The ring
 // holds the tile's first passes on entry.
-template <int FMT, int CB, int B, int G, int S, int R, bool XL, int D>
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool PAIR, int D>
 __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
                                           int64_t row0, const int (&q)[8], const uint16_t* x, int x_per_slot,
-                                          int64_t topk, float* y, float gmul, float* red, uint8_t* xlds,
-                                          RowCursor<R>& cur, PassRing<RowPass<FMT, CB, R>, D + 1>& ring) {
+                                          int64_t topk, float* y, uint16_t* act, float gmul, float* red,
+                                          uint8_t* xlds, RowCursor<R>& cur,
+                                          PassRing<RowPass<FMT, CB, R>, D + 1>& ring) {
     const uint16_t* xs[B];
     float* ys[B];
 #pragma unroll
@@ -77,7 +78,9 @@ __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* s
         ys[b] = q[b] >= 0 ? y + (int64_t)q[b] * n : nullptr;
     }
     if constexpr (XL) stage_x<FMT, CB, B>(xs, k, xlds);
-    const RowEngine<FMT, CB, B, G, S, R, XL> eng(codes, scales, n, k);
+    RowEngine<FMT, CB, B, G, S, R, XL, false, false, PAIR> eng(codes, scales, n, k);
+    eng.y0 = y;
+    eng.act0 = act;
     eng.template run<D>(cur, ring, xs, ys, gmul, red, xlds);
 }
 
@@ -85,14 +88,21 @@ __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* s
 // Every wave reads the routing ids itself (two per lane) and finds, with
 // ballots, whether an earlier position holds the same expert and which later
 // positions share it: no LDS and no barrier before the weight loads start.
-template <int FMT, int CB, int G, int S, int R, bool XL, int RC>
-__global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict__ codes,
+// PAIR: the rows are a SwiGLU layer's gate rows then up rows, and position q
+// also gets its activations bf16(silu(gate) * up) at act + q n/2 (a position
+// with an invalid id gets NaN outputs and no activations).
+// At least 3 waves per SIMD: the two-vector loops sit just under the 170
+// registers that allow 3 (a few more registers would halve the waves in
+// flight: MI355X, 30B-A3B gate/up with SwiGLU, 2 tokens 8 -> 12 us).
+template <int FMT, int CB, int G, int S, int R, bool XL, int RC, bool PAIR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void moe_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gscale,
                                                        const int32_t* __restrict__ ids,
                                                        const uint16_t* __restrict__ x, int x_per_slot,
-                                                       float* __restrict__ y, int64_t experts, int64_t n, int64_t k,
-                                                       int pairs, int64_t topk) {
+                                                       float* __restrict__ y, uint16_t* __restrict__ act,
+                                                       int64_t experts, int64_t n, int64_t k, int pairs,
+                                                       int64_t topk) {
     using T = RowTile<G, S, R>;
     __shared__ float red[S > 1 ? S * T::ROWSETS * R * 8 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict
     const uint8_t* ecodes = codes + (int64_t)e * n * rowbytes;
     const uint8_t* escales = scales + (int64_t)e * n * (k / BlockSize<FMT>::value);
     // Weights first: the first passes are in flight while the activations load.
-    using Geo = RowEngine<FMT, CB, 1, G, S, R, XL>;
+    using Geo = RowEngine<FMT, CB, 1, G, S, R, XL, false, false, PAIR>;
     const Geo geo(ecodes, escales, n, k);
     RowCursor<R> cur = geo.cursor(row0, 0, 1, x);
     const RowCursor<R> start = cur;
@@ -139,40 +149,40 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict
         // the batch sizes up to RC are compiled, so a one-token launch keeps
         // the registers of a one-vector loop
         if (RC == 1 || q[1] < 0) {
-            moe_round<FMT, CB, 1, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+            moe_round<FMT, CB, 1, G, S, R, XL, PAIR, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, act, gmul, red, xlds, cur, ring);
         } else if constexpr (RC >= 2) {
             if (RC == 2 || q[2] < 0) {
-                moe_round<FMT, CB, 2, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+                moe_round<FMT, CB, 2, G, S, R, XL, PAIR, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, act, gmul, red, xlds, cur, ring);
             } else if constexpr (RC >= 4) {
                 if (RC == 4 || q[4] < 0)
-                    moe_round<FMT, CB, 4, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+                    moe_round<FMT, CB, 4, G, S, R, XL, PAIR, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, act, gmul, red, xlds, cur, ring);
                 else
-                    moe_round<FMT, CB, 8, G, S, R, XL, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, gmul, red, xlds, cur, ring);
+                    moe_round<FMT, CB, 8, G, S, R, XL, PAIR, kMoeAhead>(ecodes, escales, n, k, row0, q, x, x_per_slot, topk, y, act, gmul, red, xlds, cur, ring);
             }
         }
     }
 }
 
-template <int FMT, int CB, int G, int S, int R, int RC>
+template <int FMT, int CB, int G, int S, int R, int RC, bool PAIR>
 static void launch_moe_rc(const MoeArgs& a, hipStream_t st) {
     using T = RowTile<G, S, R>;
     const int64_t tiles = (a.n + T::ROWS - 1) / T::ROWS;
     const int pairs = (int)(a.tokens * a.topk);
     const int64_t lds = x_lds_bytes<FMT, CB>(a.k, RC);
     if (lds <= kMoeMaxXLds)
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true, RC>), dim3((unsigned)tiles, (unsigned)pairs),
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true, RC, PAIR>), dim3((unsigned)tiles, (unsigned)pairs),
                            dim3(kThreads), (size_t)lds, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
-                           a.experts, a.n, a.k, pairs, a.topk);
+                           a.act, a.experts, a.n, a.k, pairs, a.topk);
     else
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false, RC>), dim3((unsigned)tiles, (unsigned)pairs),
-                           dim3(kThreads), 0, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false, RC, PAIR>), dim3((unsigned)tiles, (unsigned)pairs),
+                           dim3(kThreads), 0, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y, a.act,
                            a.experts, a.n, a.k, pairs, a.topk);
 }
 
-template <int FMT, int CB, int G, int S, int R>
+template <int FMT, int CB, int G, int S, int R, bool PAIR = false>
 static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
-    if (moe_round_cap(a.tokens) == 1) launch_moe_rc<FMT, CB, G, S, R, 1>(a, st);
-    else launch_moe_rc<FMT, CB, G, S, R, 2>(a, st);
+    if (moe_round_cap(a.tokens) == 1) launch_moe_rc<FMT, CB, G, S, R, 1, PAIR>(a, st);
+    else launch_moe_rc<FMT, CB, G, S, R, 2, PAIR>(a, st);
 }
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
@@ -183,6 +193,14 @@ static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
 template <int FMT, int CB>
 static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
+    if (a.act) {
+        // SwiGLU pairs: two rows per lane, the lanes per row of the plain shapes
+        if (a.n % 2) return false;
+        if (nchunks >= 64 && a.tokens <= 4) launch_moe_inst<FMT, CB, 16, 1, 2, true>(a, st);
+        else if (nchunks >= 8) launch_moe_inst<FMT, CB, 8, 1, 2, true>(a, st);
+        else launch_moe_inst<FMT, CB, 4, 1, 2, true>(a, st);
+        return true;
+    }
     int g = 16, sp = 1, r = 2;
     if (nchunks < 64) {
         r = 1;

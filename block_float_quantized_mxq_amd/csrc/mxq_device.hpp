@@ -140,6 +140,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
+// SwiGLU activation a = bf16(silu(g) * u) with silu(g) = g / (1 + e^-g), in
+// fp32, the product rounded to the nearest bf16 (ties to even).  Below
+// g = -64, 1 + e^-g equals e^-g far beyond fp32 precision (e^-64 < 2^-92),
+// and from g = -88.7 e^-g overflows (the quotient would become 0 while
+// silu(g) is still a normal fp32 number), so there silu(g) = g e^g is formed
+// as (g e^(g/2)) e^(g/2): g/2 is exact, both factors stay normal down to
+// g = -174, and the result is within a few ulp (zero below that, as it is
+// in fp32).
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u) {
+    float s;
+    if (g >= -64.0f) {
+        s = g / (1.0f + expf(-g));
+    } else {
+        const float e = expf(0.5f * g);
+        s = g * e * e;
+    }
+    return __builtin_bit_cast(uint16_t, (__bf16)(s * u));
+}
+
 // DPP controls (GFX9 encoding).
 enum : int { kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140 };
 

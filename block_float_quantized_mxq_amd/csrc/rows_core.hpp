@@ -243,7 +243,14 @@ struct RowCursor {
 // 12 of each 16 are discarded); they are added by one quad reduction at the
 // end of the tile.  The vector ALU only decodes, so batch 4 costs what batch 1
 // does; S splits k across the waves of the workgroup.
-template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool SLOTS = false, bool MM = false>
+//
+// Paired mode (PAIR): the tile's rows are taken in pairs, logical row 2i + h
+// being physical row i + h * n/2 (n even), so each lane holds the gate row i
+// and the up row i of a SwiGLU layer (gate rows first, up rows second); the
+// tile's end stores both products and, to `act`, the activation
+// bf16(silu(gate) * up).
+template <int FMT, int CB, int B, int G, int S, int R, bool XL, bool SLOTS = false, bool MM = false,
+          bool PAIR = false>
 struct RowEngine {
     using CS = ChunkShape<FMT, CB>;
     using T = RowTile<G, S, R>;
@@ -252,6 +259,7 @@ struct RowEngine {
     using Cursor = RowCursor<R>;
     static_assert(!MM || (G == 16 && B <= 4 && !SLOTS && (S == 1 || S == 2 || S == 4)),
                   "matrix mode: 16 chunk positions, batch <= 4, k split across the 4 waves");
+    static_assert(!PAIR || (S == 1 && R % 2 == 0 && !SLOTS && !MM), "paired rows: one k group, rows in pairs");
     static constexpr int NA = MM ? 4 : B;  // accumulators per row (MM: the 4 rows of an MFMA block)
     static constexpr int RED_FLOATS = S > 1 ? S * T::ROWSETS * R * NA : 1;
     static constexpr int WSETS = 4 / S;    // MM: wave row groups per workgroup
@@ -260,6 +268,9 @@ struct RowEngine {
     const uint8_t* scales;
     int64_t n, rowbytes, sbytes, nchunks, step, c0, niter;
     int lane, rs, sp, mi;
+    // PAIR: output ys[b] = y0 + q n is position q; its activations go to act0 + q n/2
+    const float* y0 = nullptr;
+    uint16_t* act0 = nullptr;
 
     __device__ __forceinline__ RowEngine(const uint8_t* codes_, const uint8_t* scales_, int64_t n_, int64_t k) {
         codes = codes_;
@@ -295,6 +306,7 @@ struct RowEngine {
         for (int j = 0; j < R; ++j) {
             int64_t r = MM ? row0 + (int64_t)rs * 4 * R + 4 * j + mi : row0 + (int64_t)rs * R + j;
             r = r < n ? r : n - 1;
+            if constexpr (PAIR) r = (r >> 1) + (r & 1) * (n >> 1);
             p.c[j] = codes + r * rowbytes;
             p.s[j] = scales + r * sbytes;
         }
@@ -496,7 +508,26 @@ struct RowEngine {
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[j][b] = group_sum<G>(acc[j][b]);
 
-        if constexpr (S == 1) {
+        if constexpr (PAIR) {
+            if (lane == 0) {
+                const int64_t half = n >> 1;
+#pragma unroll
+                for (int j = 0; j < R; j += 2) {
+                    const int64_t i = (row0 + (int64_t)rs * R + j) >> 1;
+                    if (i < half) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            if (ys[b]) {
+                                const float g = acc[j][b] * gmul, u = acc[j + 1][b] * gmul;
+                                ys[b][i] = g;
+                                ys[b][i + half] = u;
+                                act0[(ys[b] - y0) / 2 + i] = swiglu_bf16(g, u);
+                            }
+                        }
+                    }
+                }
+            }
+        } else if constexpr (S == 1) {
             if (lane == 0) {
 #pragma unroll
                 for (int j = 0; j < R; ++j) {

@@ -220,17 +220,20 @@ mxq_status_t mxq_moe_route(const float *logits, int32_t *expert_ids, float *weig
  *                                                       rounded to nearest even
  *   y[t][i]    = sum_s weights[t][s] * sum_j W_dn[ids[t][s]][i][j] * a[t][s][j]
  *
- * Kernel 1 is mxq_moe_gemv on the gate/up bank (each routed expert read once,
- * into the caller's workspace h); kernel 2 builds the activations in LDS and
- * streams each output row of the token's routed down matrices, combining them
- * in a fixed order.  A token with an expert id outside [0, num_experts) gets
- * NaN outputs.
+ * Kernel 1 is the expert-indexed GEMV of mxq_moe_gemv on the gate/up bank
+ * (each routed expert read once) with gate row j and up row j in one lane: it
+ * writes h and the activations a into the caller's workspace; kernel 2 copies
+ * a token's activations into LDS and streams each output row of the token's
+ * routed down matrices, combining them in a fixed order.  A token with an
+ * expert id outside [0, num_experts) gets NaN outputs.
  *   gu_codes/gu_scales  gate/up bank [num_experts][2*dff][hidden] (layout as mxq_moe_gemv)
  *   dn_codes/dn_scales  down bank [num_experts][hidden][dff]
  *   gu_gscale/dn_gscale NVFP4: fp32 [num_experts] each; MX: NULL
  *   expert_ids int32 [tokens][topk]; weights fp32 [tokens][topk]
  *   x        bf16 [tokens][hidden]
- *   h        fp32 [tokens][topk][2*dff] workspace (caller-owned, 16-byte aligned)
+ *   h        workspace of tokens*topk*dff*10 bytes (caller-owned, 16-byte
+ *            aligned): fp32 h [tokens][topk][2*dff], then bf16 a
+ *            [tokens][topk][dff]; both are left holding the call's values
  *   y        fp32 [tokens][hidden]
  *   hidden, dff multiples of the block size (32 MX, 16 NVFP4); tokens 1 .. MXQ_MAX_BATCH;
  *   topk 1 .. MXQ_MAX_TOPK with topk rounded up to a power of two, times 2*dff
@@ -246,16 +249,16 @@ mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_s
  * Allocation-free MoE decode block, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same computation, kernels and arguments as
- * mxq_moe_block without `h`; the gate/up outputs go to a static device array
- * of 2 MiB that the library holds on each GPU it runs on until the process
- * ends (looked up once per device; the call allocates nothing).
- *   tokens * topk * 2 * dff * 4 bytes at most 2 MiB (every call the LDS limit
+ * mxq_moe_block without `h`; the workspace (h and a) goes to a static device
+ * array of 2.5 MiB that the library holds on each GPU it runs on until the
+ * process ends (looked up once per device; the call allocates nothing).
+ *   tokens * topk * dff * 10 bytes at most 2.5 MiB (every call the LDS limit
  *   above admits fits), else MXQ_E_UNSUPPORTED; MXQ_E_DEVICE if the array's
  *   address cannot be obtained.
  * All calls on one GPU share the array: calls that overlap in time on one GPU
  * (different streams, or several host threads) race and must be serialised
- * by the caller.  The array needs no clearing (h is written in full before it
- * is read).
+ * by the caller.  The array needs no clearing (each call writes the parts it
+ * reads before reading them).
  */
 mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales,
                                    const float *gu_gscale, const uint8_t *dn_codes, const uint8_t *dn_scales,
@@ -356,7 +359,7 @@ mxq_status_t mxq_stream_read(const void *data, int64_t bytes, int layout, uint32
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 7 (6 plus mxq_stream_read). */
+/* ABI version of this header: 8 (7 with the MoE block workspace grown to hold the activations). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

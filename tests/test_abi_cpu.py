@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 7
+    assert lib.mxq_abi_version() == 8
 
 
 def test_status_strings():
@@ -232,7 +232,7 @@ def test_device_error_without_gpu():
     assert mgemm(m=(1 << 24) // 8, topk=8, E=1024, k=4064) == DEVICE  # largest accepted sizes
     assert quant() == DEVICE and quant(fmt=3, g=A, k=48) == DEVICE and quant(rows=1 << 20, k=1 << 16) == DEVICE
     assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
-    # the largest workspace every admitted call needs (8 tokens x 16 slots x 2 x 2048 floats) fits the array
+    # the largest workspace every admitted call needs (8 tokens x 16 slots x 2048 columns x 10 bytes) fits the array
     assert block_na() == DEVICE and block_na(T=8, topk=16, dff=2048, E=16) == DEVICE
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
     assert requant() == DEVICE and requant(n=1 << 20, k=1 << 16, bn=1, bk=32) == DEVICE

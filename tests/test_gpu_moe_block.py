@@ -73,16 +73,36 @@ def test_route_infinite_logits():
 
 # ---- the block ------------------------------------------------------------------------
 
-def run_block(c, ids=None, h=None):
+def run_block(c, ids=None, act=False):
+    """y, the gate/up workspace h [T, topk, 2 dff] (and with act the bf16 activations as float32)."""
     ids = c["ids"] if ids is None else ids
     gc, gs, gg = c["gu"]
     dc, ds, dg = c["dn"]
     T, topk = ids.shape
-    if h is None:
-        h = torch.full((T, topk, 2 * c["dff"]), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws = torch.full((mxq.moe_block_workspace_elems(T, topk, c["dff"]),), float("nan"), dtype=torch.float32,
+                    device="cuda:0")
     y = mxq.moe_block(c["fmt"], dev_u8(gc), dev_u8(gs), dev_u8(dc), dev_u8(ds), dev_i32(ids), dev_f32(c["w"]),
-                      dev_bf16(c["x"]), gu_global_scale=dev_f32(gg), dn_global_scale=dev_f32(dg), h=h)
-    return host(y), host(h)
+                      dev_bf16(c["x"]), gu_global_scale=dev_f32(gg), dn_global_scale=dev_f32(dg), h=ws)
+    h, a = mxq.moe_block_workspace_views(ws, T, topk, c["dff"])
+    return (host(y), host(h), host(a.float())) if act else (host(y), host(h))
+
+
+def check_activations(h, a, what):
+    """The activations the gate/up kernel wrote against the oracle's SwiGLU of the kernel's own gate/up values:
+    bf16(fl32(fl32(silu(g)) * u)), either neighbour accepted where the fp32 product is within 8 fp32 ulp of a
+    bf16 tie (the kernel's fp32 exp and division differ from the exact silu by a few ulp)."""
+    dff = h.shape[-1] // 2
+    g, u = h[..., :dff].reshape(-1), h[..., dff:].reshape(-1)
+    a = a.reshape(-1)
+    valid = np.isfinite(g) & np.isfinite(u)
+    assert valid.any(), f"{what}: no finite gate/up values"
+    bad = []
+    for i in np.flatnonzero(valid):
+        p = float(np.float32(np.float32(oracle.silu(float(g[i]))) * u[i]))
+        lo, hi = oracle.round_bf16(p - abs(p) * 2.0 ** -21), oracle.round_bf16(p + abs(p) * 2.0 ** -21)
+        if not (min(lo, hi) <= a[i] <= max(lo, hi)):
+            bad.append((i, g[i], u[i], a[i], oracle.round_bf16(p)))
+    assert not bad, f"{what}: {len(bad)} activations off the oracle's SwiGLU, first {bad[:3]}"
 
 
 def reference(c, tol, ids=None):
@@ -98,7 +118,8 @@ def gate_up_reference(c, ids=None):
 
 def check_block(c, what, exact, ids=None):
     say(what)
-    y, h = run_block(c, ids)
+    y, h, a = run_block(c, ids, act=True)
+    check_activations(h, a, what)
     h_ref, h_abs = gate_up_reference(c, ids)
     if exact:
         h32 = h_ref.astype(np.float32)

@@ -1,5 +1,5 @@
-"""mxq_moe_block_noalloc (the MoE decode block with its gate/up workspace in the
-library's static device array) against mxq_moe_block (caller workspace) and the
+"""mxq_moe_block_noalloc (the MoE decode block with its workspace -- gate/up
+outputs and activations -- in the library's static device array) against mxq_moe_block (caller workspace) and the
 oracle: two calls in a row, the second smaller, so the second call runs on the
 array the first one left behind."""
 import numpy as np
@@ -36,9 +36,9 @@ def _check(c, what):
 
 
 def test_noalloc_block_two_calls_second_smaller():
-    # first call: 8 tokens of the 30B-A3B-like block (h = 8 x 8 x 1536 floats)
+    # first call: 8 tokens of the 30B-A3B-like block (workspace 8 x 8 x 768 x 10 bytes)
     _check(synth.moe_block(8, seed=41, exact=True), "noalloc block T=8 H=2048 dff=768 top-8")
-    # second call: fewer tokens, narrower experts (h = 2 x 4 x 512 floats)
+    # second call: fewer tokens, narrower experts (workspace 2 x 4 x 256 x 10 bytes)
     _check(synth.moe_block(2, seed=42, experts=16, hidden=512, dff=256, topk=4, exact=True),
            "noalloc block T=2 H=512 dff=256 top-4")
 
