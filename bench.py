@@ -304,9 +304,25 @@ def main():
                 us = ms * 1e3 / nsets
                 r = dict(us=us, active_mb=float(active.mean() / 1e6), gbs=float(active.mean() / (us * 1e-6) / 1e9))
                 r["pct_peak"] = 100 * r["gbs"] / PEAK_HBM_GBS
+                # time breakdown: one bank and one id set repeated (the routed experts stay in the caches),
+                # and every id invalid (launch, id read and NaN stores: the kernel's floor)
+                bad = torch.full((T, 8), -1, dtype=torch.int32, device=dev)
+
+                def fn_resident():
+                    for _ in range(nsets):
+                        mxq.moe_gemv(1, *banks[0], ids_dev[0], x, per_slot, out=y)
+
+                def fn_floor():
+                    for _ in range(nsets):
+                        mxq.moe_gemv(1, *banks[0], bad, x, per_slot, out=y)
+
+                r["resident_us"] = timed_graph(fn_resident, 8) * 1e3 / nsets
+                r["invalid_ids_floor_us"] = timed_graph(fn_floor, 8) * 1e3 / nsets
                 moe[f"{which}_T{T}"] = r
-                log(f"moe {which} T={T}: {us:.2f} us, {r['active_mb']:.1f} MB active, {r['gbs']:.0f} GB/s")
+                log(f"moe {which} T={T}: {us:.2f} us, {r['active_mb']:.1f} MB active, {r['gbs']:.0f} GB/s; "
+                    f"cache-resident {r['resident_us']:.2f} us, invalid-ids floor {r['invalid_ids_floor_us']:.2f} us")
                 # config 3 check: the last id set's outputs, all of them
+                mxq.moe_gemv(1, *banks[-1], ids_dev[-1], x, per_slot, out=y)
                 pending[f"moe_{which}_T{T}"] = ("moe_gemv", (1, case["codes"], case["scales"], None, idsets[-1], xh,
                                                              per_slot, 128, n, k),
                                                 y.cpu().numpy(), f"all {T * 8 * n}",

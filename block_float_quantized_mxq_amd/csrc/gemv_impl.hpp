@@ -156,18 +156,23 @@ static bool launch_rows_b(const GemvArgs& a, const GemvConfig& cfg, hipStream_t 
 
 // Matrix mode (rows_core.hpp, MM) for batches 2 .. 4.  Settings measured on
 // MI355X over the dense shapes (gate/up 51200 x 5120, down 5120 x 25600, QKV
-// 7168 x 5120): k split across 2 waves, or 4 for rows of 1024 chunks and more;
+// 7168 x 5120): k split across 2 waves, or 4 for rows of 512 chunks and more;
 // 4 four-row groups per lane from batch 3 on long or many rows, else 2.  Batch
 // 4: gate/up 41.6 -> 27.8 us, down 39.5 -> 23.1 us, QKV 10.9 -> 9.2 us against
-// the FMA mode; batch 2: gate/up 27.6 -> 25.4 us, down 23.8 -> 18.7 us.
+// the FMA mode; batch 2: gate/up 27.6 -> 25.4 us, down 23.8 -> 18.7 us.  For
+// down (800 chunks) the 4-way split beats the 2-way one at both batches
+// (batch 2: 26.1 -> 19.7 us; batch 4: 27.2 -> 23.1 us with 4 groups per lane).
+// A batch-4 down row set reads its activations from global memory (4 x 25600
+// bf16 do not fit the LDS); carrying them with the passes, loaded as far ahead
+// as the weights, measured slower (23.1 -> 24.8 us), so they are read on use.
 template <int FMT, int CB, int B>
 static bool launch_rows_mm(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st) {
     int sp = cfg.mm_s, r = cfg.mm_r;
     const int64_t occ = cfg.rows_occ > 0 ? cfg.rows_occ : 8;
     if (sp == 0 || r == 0) {
         const int64_t nchunks = code_bytes_per_row(FMT, a.k) / CB;
-        sp = nchunks >= 1024 ? 4 : 2;
-        r = (a.batch >= 3 && (a.n >= 16384 || nchunks >= 1024)) ? 4 : 2;
+        sp = nchunks >= 512 ? 4 : 2;
+        r = (a.batch >= 3 && (a.n >= 16384 || nchunks >= 512)) ? 4 : 2;
     }
 #define MXQ_MM_CASE(S_, R_)                                                    \
     if (sp == S_ && r == R_) {                                                \
