@@ -441,6 +441,19 @@ def main():
                                       y32, "64 seeded rows x 25600", sha256(c["codes"], c["scales"], c["x"], c["rows"]))
         del codes, scales, X, Y, Y32
         torch.cuda.empty_cache()
+        # the other formats on the same shape (the same bf16 MFMA; MXFP8 streams 32-k slices)
+        fm = {}
+        for fmt, name in ((mxq.MXFP8, "mxfp8"), (mxq.NVFP4, "nvfp4")):
+            cf = synth.prefill(seed=0, fmt=fmt)
+            codes, scales, X = u8(cf["codes"]), u8(cf["scales"]), bf(cf["x"])
+            g = None if cf["g"] is None else torch.from_numpy(cf["g"]).to(dev)
+            Y = torch.empty((cf["m"], cf["n"]), dtype=torch.bfloat16, device=dev)
+            fms = timed_graph(lambda: mxq.gemm(fmt, codes, scales, X, g, out=Y), 5)
+            fm[name] = dict(ms=round(fms, 4), tflops=round(flops / (fms * 1e-3) / 1e12, 1))
+            log(f"gemm {name}: {fms:.3f} ms, {fm[name]['tflops']:.1f} TFLOP/s")
+            del codes, scales, X, Y, cf
+            torch.cuda.empty_cache()
+        extras["prefill_gemm"]["formats"] = fm
 
     # ---------------- expert-batched MoE prefill GEMM ----------------
     if "moe_gemm" in parts:

@@ -27,30 +27,34 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// One lane's W codes for one slice: the 32 consecutive k of one row starting
-// at a multiple of 32, and their scale byte(s).
-template <int FMT>
+// One lane's W codes for one slice: the KE (32, or 16 for E4M3) consecutive k
+// of one row starting at a multiple of KE, and their scale byte(s).
+template <int FMT, int KE = 32>
 struct WFrag {
-    static constexpr int DW = (FMT == kMXFP8) ? 8 : 4;
+    static_assert(KE == 32 || (KE == 16 && FMT == kMXFP8), "32 elements, or 16 of E4M3 (16 bytes)");
+    static constexpr int DW = (FMT == kMXFP8) ? KE / 4 : 4;
     uint32_t w[DW];
     uint32_t s;  // one E8M0 byte, or two E4M3 bytes (NVFP4) in bits 7:0 and 15:8
 };
 
 // Elements past k read as zero codes (with a unit scale).
-template <int FMT>
+template <int FMT, int KE>
 __device__ __forceinline__ void load_wfrag(const uint8_t* crow, const uint8_t* srow, int64_t kb, int64_t k,
-                                           WFrag<FMT>& f) {
+                                           WFrag<FMT, KE>& f) {
     if (kb >= k) {
 #pragma unroll
-        for (int i = 0; i < WFrag<FMT>::DW; ++i) f.w[i] = 0u;
+        for (int i = 0; i < WFrag<FMT, KE>::DW; ++i) f.w[i] = 0u;
         f.s = FMT == kNVFP4 ? 0x3838u : 127u;
         return;
     }
     if constexpr (FMT == kMXFP8) {
         const u32x4g_t* q = reinterpret_cast<const u32x4g_t*>(crow + kb);
-        const u32x4g_t v0 = q[0], v1 = q[1];
+        const u32x4g_t v0 = q[0];
         f.w[0] = v0[0]; f.w[1] = v0[1]; f.w[2] = v0[2]; f.w[3] = v0[3];
-        f.w[4] = v1[0]; f.w[5] = v1[1]; f.w[6] = v1[2]; f.w[7] = v1[3];
+        if constexpr (KE == 32) {
+            const u32x4g_t v1 = q[1];
+            f.w[4] = v1[0]; f.w[5] = v1[1]; f.w[6] = v1[2]; f.w[7] = v1[3];
+        }
         f.s = srow[kb / 32];
     } else {
         const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kb / 2);
@@ -61,8 +65,9 @@ __device__ __forceinline__ void load_wfrag(const uint8_t* crow, const uint8_t* s
 }
 
 // The B operand of k step S: the fragment's codes S*8 .. S*8+7 as bf16.
-template <int FMT, int S>
-__device__ __forceinline__ bf16x8_t decode_step(const WFrag<FMT>& f) {
+template <int FMT, int S, int KE>
+__device__ __forceinline__ bf16x8_t decode_step(const WFrag<FMT, KE>& f) {
+    static_assert(S * 8 < KE, "k step inside the fragment");
     uint32_t d[4];
     if constexpr (FMT == kMXFP4) {
         const float se = e8m0_exponent(f.s);
@@ -94,19 +99,19 @@ __device__ __forceinline__ bf16x8_t decode_step(const WFrag<FMT>& f) {
 // other fragments' codes zeroed, lifted fragments decoded with byte
 // u + kMx8Lift).  The plain part goes into the accumulator as usual; the
 // lifted part into a separate sum that is multiplied by 2^-kMx8Lift in fp32.
-template <int FMT>
-__device__ __forceinline__ bool frag_lifted(const WFrag<FMT>& f) {
+template <int FMT, int KE>
+__device__ __forceinline__ bool frag_lifted(const WFrag<FMT, KE>& f) {
     return mx_lifted<FMT>(f.s);
 }
 
-template <int FMT, int S, bool LIFTED>
-__device__ __forceinline__ bf16x8_t decode_step_part(const WFrag<FMT>& f) {
+template <int FMT, int S, bool LIFTED, int KE>
+__device__ __forceinline__ bf16x8_t decode_step_part(const WFrag<FMT, KE>& f) {
     static_assert(FMT == kMXFP8, "only MXFP8 fragments are lifted");
-    const bool lo = frag_lifted<FMT>(f);
+    const bool lo = frag_lifted(f);
     const bool keep = LIFTED ? lo : !lo;
-    WFrag<FMT> g;
+    WFrag<FMT, KE> g;
 #pragma unroll
-    for (int d = 0; d < WFrag<FMT>::DW; ++d) g.w[d] = keep ? f.w[d] : 0u;
+    for (int d = 0; d < WFrag<FMT, KE>::DW; ++d) g.w[d] = keep ? f.w[d] : 0u;
     g.s = LIFTED ? (lo ? f.s + kMx8Lift : 127u) : f.s;
     return decode_step<FMT, S>(g);
 }

@@ -44,11 +44,22 @@ namespace mxq {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBN = 256;
 constexpr int kGemmThreads = 512;
-constexpr int kXStride = kBK + 8;                         // bf16 elements per LDS row of X
-constexpr int kXTileElems = kBM * kXStride;               // per buffer
-constexpr int kXPieces = kBM * kBK / 8 / kGemmThreads;    // 16-byte X pieces per thread per slice
+
+// Slice shape per format: 64 k (each lane's W share one 32-element block,
+// 16 bytes of E2M1 codes), or 32 k for E4M3 (a 16-element half block, 16
+// bytes: a 32-byte share leaves too few registers for the pipelined slices).
+template <int FMT>
+struct GemmSlice {
+    static constexpr int BK = FMT == kMXFP8 ? 32 : 64;
+    static constexpr int KE = BK / 2;                         // k per lane per fragment
+    static constexpr int STEPS = BK / 16;                     // MFMA k steps per slice
+    static constexpr int XSTRIDE = BK + 8;                    // bf16 per LDS row of X (16-byte pad)
+    static constexpr int XTILE = kBM * XSTRIDE;               // per buffer
+    static constexpr int PPR = BK / 8;                        // 16-byte pieces per row
+    static constexpr int XPIECES = kBM * BK / 8 / kGemmThreads;
+};
 
 // Tile coordinates of workgroup b (XCD-aware grouped order): consecutive
 // "local" indices of one XCD walk a GM-tall column strip of tiles, n fastest.
@@ -74,6 +85,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
                                                             const uint16_t* __restrict__ x, void* __restrict__ yv,
                                                             int y_bf16, int64_t m, int64_t n, int64_t k,
                                                             int xcd_order) {
+    using GS = GemmSlice<FMT>;
+    constexpr int kBK = GS::BK, kXStride = GS::XSTRIDE, kXTileElems = GS::XTILE, kXPieces = GS::XPIECES;
+    constexpr int kPPR = GS::PPR;
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_lds[];  // [2][kBM][kXStride]
 
     const int tid = threadIdx.x;
@@ -89,14 +103,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
     const int64_t rowbytes = code_bytes_per_row(FMT, k);
     const int64_t sbytes = k / block_elems(FMT);
 
-    // X loader: piece p = tid + 256*u is row p/8, 16-byte column p%8 of the slice.
+    // X loader: piece p = tid + kGemmThreads*u is row p/kPPR, 16-byte column p%kPPR of the slice.
     const uint16_t* xrow[kXPieces];
 #pragma unroll
     for (int u = 0; u < kXPieces; ++u) {
         const int p = tid + kGemmThreads * u;
-        int64_t r = m0 + (p >> 3);
+        int64_t r = m0 + p / kPPR;
         r = r < m ? r : m - 1;  // rows past m read row m-1; their outputs are not written
-        xrow[u] = x + r * k + (p & 7) * 8;
+        xrow[u] = x + r * k + (p % kPPR) * 8;
     }
     // W rows of this lane's two fragments (columns wn*64 + j*32 + l32).
     const uint8_t* crow[2];
@@ -114,7 +128,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
 #pragma unroll
         for (int u = 0; u < kXPieces; ++u) {
             const int p = tid + kGemmThreads * u;
-            if (k0 + (p & 7) * 8 < k) xr[u] = *reinterpret_cast<const u32x4g_t*>(xrow[u] + k0);
+            if (k0 + (p % kPPR) * 8 < k) xr[u] = *reinterpret_cast<const u32x4g_t*>(xrow[u] + k0);
             else xr[u] = u32x4g_t{0u, 0u, 0u, 0u};
         }
     };
@@ -123,12 +137,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
 #pragma unroll
         for (int u = 0; u < kXPieces; ++u) {
             const int p = tid + kGemmThreads * u;
-            *reinterpret_cast<u32x4g_t*>(dst + (p >> 3) * kXStride + (p & 7) * 8) = xr[u];
+            *reinterpret_cast<u32x4g_t*>(dst + (p / kPPR) * kXStride + (p % kPPR) * 8) = xr[u];
         }
     };
-    auto load_w = [&](int64_t k0, WFrag<FMT> (&wf)[2]) {
+    using Frag = WFrag<FMT, GS::KE>;
+    auto load_w = [&](int64_t k0, Frag (&wf)[2]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load_wfrag<FMT>(crow[j], srow[j], k0 + half * 32, k, wf[j]);
+        for (int j = 0; j < 2; ++j) load_wfrag(crow[j], srow[j], k0 + half * GS::KE, k, wf[j]);
     };
 
     f32x16_t acc[4][2];
@@ -141,15 +156,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
 
     // The MFMAs of one slice: A from LDS buffer `buf`, B decoded from wf.  The
     // operands of k step s+1 are read and decoded before the MFMAs of step s.
-    auto mfma_slice = [&](int buf, const WFrag<FMT>(&wf)[2]) {
-        const uint16_t* as = xs_lds + buf * kXTileElems + (wm * 128 + l32) * kXStride + half * 32;
+    auto mfma_slice = [&](int buf, const Frag (&wf)[2]) {
+        const uint16_t* as = xs_lds + buf * kXTileElems + (wm * 128 + l32) * kXStride + half * GS::KE;
         bf16x8_t a[2][4], b[2][2];
-        auto operands = [&](auto step, bf16x8_t(&ao)[4], bf16x8_t(&bo)[2]) {
+        auto operands = [&](auto step, bf16x8_t(&ao)[4], bf16x8_t(&bo)[2], const Frag (&wd)[2]) {
             constexpr int S = decltype(step)::value;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ao[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bo[j] = decode_step<FMT, S>(wf[j]);
+            for (int j = 0; j < 2; ++j) bo[j] = decode_step<FMT, S>(wd[j]);
         };
         auto mfmas = [&](const bf16x8_t(&ao)[4], const bf16x8_t(&bo)[2]) {
 #pragma unroll
@@ -158,44 +173,57 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[i], bo[j], acc[i][j], 0, 0, 0);
         };
-        // MXFP8 slices holding a fragment with an E8M0 byte below kMx8Lift run
-        // the split form (block_operand.hpp); the branch is uniform over the wave
-        bool split = false;
-        if constexpr (FMT == kMXFP8) split = __ballot(frag_lifted<FMT>(wf[0]) || frag_lifted<FMT>(wf[1])) != 0;
-        if (!split) {
-            operands(std::integral_constant<int, 0>{}, a[0], b[0]);
-            operands(std::integral_constant<int, 1>{}, a[1], b[1]);
+        // MXFP8 (block_operand.hpp): fragments with an E8M0 byte below kMx8Lift
+        // take part in the main MFMAs with zero codes (one code path for every
+        // slice); a wave holding one adds their lifted part afterwards.
+        Frag we[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            we[j] = wf[j];
+            if constexpr (FMT == kMXFP8) {
+                const bool lo = frag_lifted(wf[j]);
+#pragma unroll
+                for (int d = 0; d < Frag::DW; ++d) we[j].w[d] = lo ? 0u : wf[j].w[d];
+            }
+        }
+        if constexpr (GS::STEPS == 4) {
+            operands(std::integral_constant<int, 0>{}, a[0], b[0], we);
+            operands(std::integral_constant<int, 1>{}, a[1], b[1], we);
             mfmas(a[0], b[0]);
-            operands(std::integral_constant<int, 2>{}, a[0], b[0]);
+            operands(std::integral_constant<int, 2>{}, a[0], b[0], we);
             mfmas(a[1], b[1]);
-            operands(std::integral_constant<int, 3>{}, a[1], b[1]);
+            operands(std::integral_constant<int, 3>{}, a[1], b[1], we);
             mfmas(a[0], b[0]);
             mfmas(a[1], b[1]);
-        } else if constexpr (FMT == kMXFP8) {
-            // plain part into the accumulators
-            static_for<0, 4>([&](auto step) {
-                constexpr int S = decltype(step)::value;
+        } else {
+            operands(std::integral_constant<int, 0>{}, a[0], b[0], we);
+            operands(std::integral_constant<int, 1>{}, a[1], b[1], we);
+            mfmas(a[0], b[0]);
+            mfmas(a[1], b[1]);
+        }
+        if constexpr (FMT == kMXFP8) {
+            if (__ballot(frag_lifted(wf[0]) || frag_lifted(wf[1])) != 0) {
+                // lifted part (decoded 2^3 larger): the accumulators are scaled by 2^3
+                // around its MFMAs, so it accumulates in place (scaling by a power of
+                // two commutes with fp32 rounding away from overflow and subnormals)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) b[0][j] = decode_step_part<FMT, S, false>(wf[j]);
-                mfmas(a[0], b[0]);
-            });
-            // lifted part: one output tile at a time, scaled back in fp32
+                    for (int j = 0; j < 2; ++j) acc[i][j] *= 1.0f / kMx8Unlift;
+                static_for<0, GS::STEPS>([&](auto step) {
+                    constexpr int S = decltype(step)::value;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                    for (int i = 0; i < 4; ++i)
+                        a[0][i] = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    f32x16_t t;
+                    for (int j = 0; j < 2; ++j) b[0][j] = decode_step_part<FMT, S, true>(wf[j]);
+                    mfmas(a[0], b[0]);
+                });
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) t[e] = 0.0f;
-                    static_for<0, 4>([&](auto step) {
-                        constexpr int S = decltype(step)::value;
-                        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(as + i * 32 * kXStride + S * 8);
-                        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, decode_step_part<FMT, S, true>(wf[j]), t, 0, 0, 0);
-                    });
-                    acc[i][j] += t * kMx8Unlift;
-                }
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] *= kMx8Unlift;
+            }
         }
     };
 
@@ -205,7 +233,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
     const int64_t nk = (k + kBK - 1) / kBK;
     const int64_t klast = (nk - 1) * kBK;
     auto kof = [&](int64_t s) { return s < nk ? s * kBK : klast; };
-    WFrag<FMT> wa[2], wb[2];
+    Frag wa[2], wb[2];
     load_x(0);
     load_w(0, wa);
     store_x(0);
@@ -255,7 +283,7 @@ static void launch_gemm_inst(const GemmArgs& a, hipStream_t st) {
     // The XCD-aware order needs the tile count to be a multiple of 8 (each
     // XCD then owns exactly tiles/8 consecutive tiles); otherwise plain order.
     const int xcd_order = (tiles % 8 == 0) ? 1 : 0;
-    const size_t lds = (size_t)2 * kXTileElems * sizeof(uint16_t);
+    const size_t lds = (size_t)2 * GemmSlice<FMT>::XTILE * sizeof(uint16_t);
     hipLaunchKernelGGL((gemm_kernel<FMT>), dim3((unsigned)tiles), dim3(kGemmThreads), lds, st, a.codes, a.scales,
                        a.gscale, a.x, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
 }

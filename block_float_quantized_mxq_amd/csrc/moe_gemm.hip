@@ -140,8 +140,8 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         w[j].s = ok ? w[j].s : (FMT == kNVFP4 ? 0x3838u : 127u);
     }
     const int64_t xstride = mfma_x_stride(k);
-    // MXFP8 weights with an E8M0 byte below kMx8Lift anywhere in the wave:
-    // every block runs the split form (block_operand.hpp); uniform over the wave
+    // MXFP8 weights with an E8M0 byte below kMx8Lift anywhere in the wave: their
+    // lifted part runs as a second pass (block_operand.hpp); uniform over the wave
     bool lifted = false;
     if constexpr (FMT == kMXFP8) {
         bool lo = false;
@@ -199,14 +199,14 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
             // (which would hold every block's operands in registers at once)
             if (j + 1 < MB) read_x(j + 1, vb[(j + 1) & 1]);
             const u32x4g_t(&v)[4] = vb[j & 1];
-            bool split = false;
-            if constexpr (FMT == kMXFP8) split = lifted;
-            if (split) {
-                if constexpr (FMT == kMXFP8) {
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
+            if constexpr (FMT == kMXFP8) {
+                // one code path: lifted blocks take part with zero codes, and a
+                // wave holding one adds their lifted part (a rare second pass)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
+                if (lifted) {
                     f32x4m_t t = {0.f, 0.f, 0.f, 0.f};
                     t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), t, 0, 0, 0);
                     t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), t, 0, 0, 0);
@@ -260,27 +260,38 @@ static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const 
 // Register blocks per lane (MB) and k split (KS): the smallest capacity
 // 4 * MB * KS blocks that holds the row, at most 8 blocks per lane (MI355X,
 // 30B-A3B gate/up bank, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us,
-// 4 x 4 179 us; its down bank: 1 x 6 93 us, 2 x 4 129 us).
+// 4 x 4 179 us; its down bank: 1 x 6 93 us, 2 x 4 129 us).  E4M3 blocks take
+// twice the registers: at most 4 per lane (6 or 8 spill), split up to 8 ways.
 template <int FMT>
 static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t pairs = a.m * a.topk;
     int32_t* goff = a.workspace;
     int32_t* gperm = a.workspace + a.experts + 1;
     const int64_t nblk = a.k / 32;
-    static constexpr int kCand[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
+    static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
+    static constexpr int kCand8[][2] = {{1, 4}, {2, 4}, {4, 4}, {8, 4}};
     int best_ks = 0, best_mb = 0;
     int64_t best_cap = 0;
-    for (const auto& c : kCand) {
-        const int64_t cap = 4LL * c[0] * c[1];
-        if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = c[0]; best_mb = c[1]; best_cap = cap; }
+    auto consider = [&](int ks, int mb) {
+        const int64_t cap = 4LL * ks * mb;
+        if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = ks; best_mb = mb; best_cap = cap; }
+    };
+    if constexpr (FMT == kMXFP8) {
+        for (const auto& c : kCand8) consider(c[0], c[1]);
+    } else {
+        for (const auto& c : kCand4) consider(c[0], c[1]);
     }
     if (best_ks == 0) return false;
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff, gperm,
                        a.y, a.y_bf16, a.n);
 #define MXQ_MG_CASE(KS_, MB_) \
     if (best_ks == KS_ && best_mb == MB_) { launch_moe_gemm_ks<FMT, KS_, MB_>(a, goff, gperm, st); return true; }
-    MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
-    MXQ_MG_CASE(4, 8)
+    if constexpr (FMT == kMXFP8) {
+        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(2, 4) MXQ_MG_CASE(4, 4) MXQ_MG_CASE(8, 4)
+    } else {
+        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
+        MXQ_MG_CASE(4, 8)
+    }
 #undef MXQ_MG_CASE
     return false;
 }

@@ -185,10 +185,11 @@ def format_sweep(fmt: int, seed: int = 0):
     return dense_layer("down", 1, seed=seed, fmt=fmt)
 
 
-def prefill(seed: int = 0, m: int = 4096, n: int = 25600, k: int = 5120, checked_rows: int = 64):
-    """bf16 token rows x MXFP4 weight (E8M0 U[120,130]) plus the seeded rows the oracle checks."""
+def prefill(seed: int = 0, m: int = 4096, n: int = 25600, k: int = 5120, checked_rows: int = 64, fmt: int = MXFP4):
+    """bf16 token rows x block-float weight (E8M0 U[120,130]; NVFP4: the default
+    E4M3 scales and per-tensor scale) plus the seeded rows the oracle checks."""
     sc, ss, sx, _, sr = streams(seed)
-    codes, scales, _ = weights(MXFP4, sc, ss, n, k, 120, 130)
+    codes, scales, g = weights(fmt, sc, ss, n, k, 120, 130)
     x = bf16_normal(sx, (m, k))
     rows = row_subset(sr, m, checked_rows)
-    return dict(fmt=MXFP4, codes=codes, scales=scales, g=None, x=x, m=m, n=n, k=k, rows=rows)
+    return dict(fmt=fmt, codes=codes, scales=scales, g=g, x=x, m=m, n=n, k=k, rows=rows)
