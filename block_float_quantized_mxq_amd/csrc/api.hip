@@ -94,7 +94,7 @@ MXQ_API const char* mxq_status_string(int s) {
 
 MXQ_API int mxq_abi_version(void) { return 8; }
 
-MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+MXQ_API mxq_status_t mxq_gemv(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
     mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
     if (st != MXQ_OK) return st;
@@ -109,7 +109,7 @@ MXQ_API mxq_status_t mxq_gemv(int fmt, const uint8_t* codes, const uint8_t* scal
     return launched(mxq::launch_gemv(a, mxq::GemvConfig{}, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_gemv_config(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+MXQ_API mxq_status_t mxq_gemv_config(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                                      const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch,
                                      const mxq_gemv_config_t* config, void* stream) {
     mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
@@ -145,7 +145,7 @@ MXQ_API mxq_status_t mxq_gemv_config(int fmt, const uint8_t* codes, const uint8_
     return launched(mxq::launch_gemv(a, cfg, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_moe_gemv(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+MXQ_API mxq_status_t mxq_moe_gemv(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                                   const int32_t* expert_ids, const uint16_t* x, int x_per_slot, float* y,
                                   int64_t num_experts, int64_t n, int64_t k, int64_t tokens, int64_t topk,
                                   void* stream) {
@@ -166,8 +166,8 @@ MXQ_API mxq_status_t mxq_moe_gemv(int fmt, const uint8_t* codes, const uint8_t* 
     return launched(mxq::launch_moe(a, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
-                              const uint16_t* x, void* y, int y_dtype, int64_t m, int64_t n, int64_t k,
+MXQ_API mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+                              const uint16_t* x, void* y, mxq_out_t y_dtype, int64_t m, int64_t n, int64_t k,
                               void* stream) {
     mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
     if (st != MXQ_OK) return st;
@@ -201,7 +201,7 @@ MXQ_API mxq_status_t mxq_gemm(int fmt, const uint8_t* codes, const uint8_t* scal
     return launched(mxq::launch_gemm(a, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+MXQ_API mxq_status_t mxq_dequant(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                                  float* w, int64_t rows, int64_t k, void* stream) {
     mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
     if (st != MXQ_OK) return st;
@@ -229,7 +229,7 @@ MXQ_API mxq_status_t mxq_moe_route(const float* logits, int32_t* expert_ids, flo
     return launched(mxq::launch_moe_route(a, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_quantize(int fmt, const uint16_t* x, const float* global_scale, uint8_t* codes,
+MXQ_API mxq_status_t mxq_quantize(mxq_format_t fmt, const uint16_t* x, const float* global_scale, uint8_t* codes,
                                   uint8_t* scales, int64_t rows, int64_t k, void* stream) {
     if (fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4) return MXQ_E_FORMAT;
     if ((fmt == MXQ_FMT_NVFP4) != (global_scale != nullptr)) return MXQ_E_FORMAT;
@@ -273,9 +273,9 @@ MXQ_API mxq_status_t mxq_stream_read(const void* data, int64_t bytes, int layout
     return launched(mxq::launch_stream_read(data, bytes, sink, want, layout, as_stream(stream)));
 }
 
-MXQ_API mxq_status_t mxq_moe_gemm(int fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
+MXQ_API mxq_status_t mxq_moe_gemm(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                                   const int32_t* expert_ids, const uint16_t* x, int x_per_slot, void* y,
-                                  int y_dtype, int32_t* workspace, int64_t num_experts, int64_t m, int64_t n,
+                                  mxq_out_t y_dtype, int32_t* workspace, int64_t num_experts, int64_t m, int64_t n,
                                   int64_t k, int64_t topk, void* stream) {
     mxq_status_t st = check_weight(fmt, codes, scales, global_scale);
     if (st != MXQ_OK) return st;
@@ -341,7 +341,7 @@ mxq_status_t run_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_s
 
 }  // namespace
 
-MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
+MXQ_API mxq_status_t mxq_moe_block(mxq_format_t fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
                                    const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
                                    const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h,
                                    float* y, int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens,
@@ -355,7 +355,7 @@ MXQ_API mxq_status_t mxq_moe_block(int fmt, const uint8_t* gu_codes, const uint8
                          y, num_experts, hidden, dff, tokens, topk, cus, stream);
 }
 
-MXQ_API mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales,
+MXQ_API mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t* gu_codes, const uint8_t* gu_scales,
                                            const float* gu_gscale, const uint8_t* dn_codes, const uint8_t* dn_scales,
                                            const float* dn_gscale, const int32_t* expert_ids, const float* weights,
                                            const uint16_t* x, float* y, int64_t num_experts, int64_t hidden,

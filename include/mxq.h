@@ -60,7 +60,11 @@
 extern "C" {
 #endif
 
-typedef enum { MXQ_FMT_MXFP4 = 1, MXQ_FMT_MXFP8 = 2, MXQ_FMT_NVFP4 = 3 } mxq_format_t;
+/* Weight formats.  The parameters that take one are typed mxq_format_t, an
+ * int, so that any value a caller passes is well defined on both sides of the
+ * ABI; values outside the enumeration are rejected with MXQ_E_FORMAT. */
+enum mxq_format { MXQ_FMT_MXFP4 = 1, MXQ_FMT_MXFP8 = 2, MXQ_FMT_NVFP4 = 3 };
+typedef int mxq_format_t;
 
 typedef enum {
     MXQ_OK = 0,
@@ -73,7 +77,9 @@ typedef enum {
     MXQ_E_LAUNCH = 7
 } mxq_status_t;
 
-typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_t;
+/* Output element types of the GEMMs (an int for the same reason). */
+enum mxq_out { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 };
+typedef int mxq_out_t;
 
 /* Largest batch of the GEMV and largest token count of the MoE GEMV. */
 #define MXQ_MAX_BATCH 8
@@ -97,7 +103,7 @@ typedef enum { MXQ_OUT_F32 = 0, MXQ_OUT_BF16 = 1 } mxq_out_t;
  *   n, k          1 <= n, k < 2^31; k % block == 0
  *   batch         1 .. MXQ_MAX_BATCH
  */
-mxq_status_t mxq_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+mxq_status_t mxq_gemv(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                       const uint16_t *x, float *y, int64_t n, int64_t k, int64_t batch, void *stream);
 
 /*
@@ -129,7 +135,7 @@ typedef struct {
     int32_t grid;
 } mxq_gemv_config_t;
 
-mxq_status_t mxq_gemv_config(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+mxq_status_t mxq_gemv_config(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                              const uint16_t *x, float *y, int64_t n, int64_t k, int64_t batch,
                              const mxq_gemv_config_t *config, void *stream);
 
@@ -152,7 +158,7 @@ mxq_status_t mxq_gemv_config(int fmt, const uint8_t *codes, const uint8_t *scale
  *   y              fp32 [tokens][topk][n]
  *   tokens         1 .. MXQ_MAX_BATCH;  topk 1 .. MXQ_MAX_TOPK
  */
-mxq_status_t mxq_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+mxq_status_t mxq_moe_gemv(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                           const int32_t *expert_ids, const uint16_t *x, int x_per_slot, float *y,
                           int64_t num_experts, int64_t n, int64_t k, int64_t tokens, int64_t topk,
                           void *stream);
@@ -177,8 +183,8 @@ mxq_status_t mxq_moe_gemv(int fmt, const uint8_t *codes, const uint8_t *scales, 
  *           from the fp32 result (MXQ_OUT_BF16)
  *   m, n, k >= 1, < 2^31; k % 32 == 0 for every format
  */
-mxq_status_t mxq_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
-                      const uint16_t *x, void *y, int y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
+mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                      const uint16_t *x, void *y, mxq_out_t y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
  * Decoded weights, for checking the in-kernel decode bit for bit:
@@ -191,7 +197,7 @@ mxq_status_t mxq_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, cons
  * times s (NVFP4); the result is exact for every code and every scale byte.
  *   w   fp32 [rows][k]
  */
-mxq_status_t mxq_dequant(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+mxq_status_t mxq_dequant(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                          float *w, int64_t rows, int64_t k, void *stream);
 
 /*
@@ -239,7 +245,7 @@ mxq_status_t mxq_moe_route(const float *logits, int32_t *expert_ids, float *weig
  *   topk 1 .. MXQ_MAX_TOPK with topk rounded up to a power of two, times 2*dff
  *   bytes, at most 64 KiB (else MXQ_E_UNSUPPORTED)
  */
-mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales, const float *gu_gscale,
+mxq_status_t mxq_moe_block(mxq_format_t fmt, const uint8_t *gu_codes, const uint8_t *gu_scales, const float *gu_gscale,
                            const uint8_t *dn_codes, const uint8_t *dn_scales, const float *dn_gscale,
                            const int32_t *expert_ids, const float *weights, const uint16_t *x, float *h, float *y,
                            int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk,
@@ -260,7 +266,7 @@ mxq_status_t mxq_moe_block(int fmt, const uint8_t *gu_codes, const uint8_t *gu_s
  * by the caller.  The array needs no clearing (each call writes the parts it
  * reads before reading them).
  */
-mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t *gu_codes, const uint8_t *gu_scales,
+mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, const uint8_t *gu_scales,
                                    const float *gu_gscale, const uint8_t *dn_codes, const uint8_t *dn_scales,
                                    const float *dn_gscale, const int32_t *expert_ids, const float *weights,
                                    const uint16_t *x, float *y, int64_t num_experts, int64_t hidden, int64_t dff,
@@ -290,8 +296,8 @@ mxq_status_t mxq_moe_block_noalloc(int fmt, const uint8_t *gu_codes, const uint8
  * kernels run on `stream` (grouping, then the GEMM); the workspace must not be
  * shared by calls that overlap.
  */
-mxq_status_t mxq_moe_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
-                          const int32_t *expert_ids, const uint16_t *x, int x_per_slot, void *y, int y_dtype,
+mxq_status_t mxq_moe_gemm(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
+                          const int32_t *expert_ids, const uint16_t *x, int x_per_slot, void *y, mxq_out_t y_dtype,
                           int32_t *workspace, int64_t num_experts, int64_t m, int64_t n, int64_t k, int64_t topk,
                           void *stream);
 
@@ -315,7 +321,7 @@ mxq_status_t mxq_moe_gemm(int fmt, const uint8_t *codes, const uint8_t *scales, 
  *   global_scale  NVFP4: device fp32 [1], input; MX: NULL
  *   k a positive multiple of the block size; rows * k <= 2^36
  */
-mxq_status_t mxq_quantize(int fmt, const uint16_t *x, const float *global_scale, uint8_t *codes, uint8_t *scales,
+mxq_status_t mxq_quantize(mxq_format_t fmt, const uint16_t *x, const float *global_scale, uint8_t *codes, uint8_t *scales,
                           int64_t rows, int64_t k, void *stream);
 
 /*
