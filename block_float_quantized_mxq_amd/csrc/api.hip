@@ -173,12 +173,15 @@ MXQ_API mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t* codes, const uint
     if (st != MXQ_OK) return st;
     if (y_dtype != MXQ_OUT_F32 && y_dtype != MXQ_OUT_BF16) return MXQ_E_FORMAT;
     if (!x || !y) return MXQ_E_NULLPTR;
-    if (m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return MXQ_E_SHAPE;
+    if (m <= 0 || n <= 0 || k <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4)) return MXQ_E_ALIGN;
     if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return MXQ_E_UNSUPPORTED;
     int cus = 0;
     if ((st = check_device(&cus)) != MXQ_OK) return st;
-    if (m <= kSmallGemmRows) {
+    // (the matrix-unit GEMV takes whole 32-element blocks: an NVFP4 k that is an
+    // odd multiple of 16 runs on the tiles at every m)
+    if (m <= kSmallGemmRows && k % 32 == 0) {
         // Few token rows: the matrix-unit GEMV with one B-operand column per
         // row streams W once per 16 rows (MI355X, 25600 x 5120: 30-50 us for
         // 1-16 rows, 90-100 us for 24-32, against 138-146 us for the 256 x 256
@@ -281,7 +284,8 @@ MXQ_API mxq_status_t mxq_moe_gemm(mxq_format_t fmt, const uint8_t* codes, const 
     if (st != MXQ_OK) return st;
     if (y_dtype != MXQ_OUT_F32 && y_dtype != MXQ_OUT_BF16) return MXQ_E_FORMAT;
     if (!expert_ids || !x || !y || !workspace) return MXQ_E_NULLPTR;
-    if (num_experts <= 0 || m <= 0 || n <= 0 || k <= 0 || topk <= 0 || k % 32 != 0) return MXQ_E_SHAPE;
+    if (num_experts <= 0 || m <= 0 || n <= 0 || k <= 0 || topk <= 0) return MXQ_E_SHAPE;
+    if ((st = check_k(fmt, k)) != MXQ_OK) return st;
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4) ||
         !aligned(expert_ids, 4) || !aligned(workspace, 4))
         return MXQ_E_ALIGN;

@@ -37,14 +37,50 @@ struct WFrag {
     uint32_t s;  // one E8M0 byte, or two E4M3 bytes (NVFP4) in bits 7:0 and 15:8
 };
 
+// NVFP4 rows whose k is an odd multiple of 16 (ROW8): rows are 8-byte aligned,
+// so the 16 bytes of a fragment come as two 8-byte loads, and the row's last
+// fragment holds one 16-element block: its second half reads as zero codes
+// with a unit scale (nothing past the row is read).
+typedef uint32_t u32x2g_t __attribute__((ext_vector_type(2)));
+
+template <bool ROW8>
+__device__ __forceinline__ void load_fp4_frag16(const uint8_t* crow, const uint8_t* srow, int64_t kb, int64_t k,
+                                                uint32_t (&w)[4], uint32_t& s) {
+    if constexpr (ROW8) {
+        const u32x2g_t* q = reinterpret_cast<const u32x2g_t*>(crow + kb / 2);
+        const u32x2g_t a = q[0];
+        w[0] = a[0];
+        w[1] = a[1];
+        if (kb + 32 <= k) {
+            const u32x2g_t b = q[1];
+            w[2] = b[0];
+            w[3] = b[1];
+            s = (uint32_t)srow[kb / 16] | ((uint32_t)srow[kb / 16 + 1] << 8);
+        } else {
+            w[2] = 0u;
+            w[3] = 0u;
+            s = (uint32_t)srow[kb / 16] | (0x38u << 8);
+        }
+    } else {
+        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kb / 2);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+        s = (uint32_t)srow[kb / 16] | ((uint32_t)srow[kb / 16 + 1] << 8);
+    }
+}
+
 // Elements past k read as zero codes (with a unit scale).
-template <int FMT, int KE>
+template <int FMT, int KE, bool ROW8 = false>
 __device__ __forceinline__ void load_wfrag(const uint8_t* crow, const uint8_t* srow, int64_t kb, int64_t k,
                                            WFrag<FMT, KE>& f) {
+    static_assert(!ROW8 || FMT == kNVFP4, "only NVFP4 rows can be 8-byte multiples");
     if (kb >= k) {
 #pragma unroll
         for (int i = 0; i < WFrag<FMT, KE>::DW; ++i) f.w[i] = 0u;
         f.s = FMT == kNVFP4 ? 0x3838u : 127u;
+        return;
+    }
+    if constexpr (FMT == kNVFP4) {
+        load_fp4_frag16<ROW8>(crow, srow, kb, k, f.w, f.s);
         return;
     }
     if constexpr (FMT == kMXFP8) {
@@ -59,8 +95,7 @@ __device__ __forceinline__ void load_wfrag(const uint8_t* crow, const uint8_t* s
     } else {
         const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kb / 2);
         f.w[0] = v[0]; f.w[1] = v[1]; f.w[2] = v[2]; f.w[3] = v[3];
-        if constexpr (FMT == kMXFP4) f.s = srow[kb / 32];
-        else f.s = (uint32_t)srow[kb / 16] | ((uint32_t)srow[kb / 16 + 1] << 8);
+        f.s = srow[kb / 32];
     }
 }
 

@@ -78,7 +78,7 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t mt, int64_t nt, int64
     tn = in / gm;
 }
 
-template <int FMT>
+template <int FMT, bool ROW8>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ gscale,
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const uint8_t* __res
     using Frag = WFrag<FMT, GS::KE>;
     auto load_w = [&](int64_t k0, Frag (&wf)[2]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load_wfrag(crow[j], srow[j], k0 + half * GS::KE, k, wf[j]);
+        for (int j = 0; j < 2; ++j) load_wfrag<FMT, GS::KE, ROW8>(crow[j], srow[j], k0 + half * GS::KE, k, wf[j]);
     };
 
     f32x16_t acc[4][2];
@@ -284,8 +284,13 @@ static void launch_gemm_inst(const GemmArgs& a, hipStream_t st) {
     // XCD then owns exactly tiles/8 consecutive tiles); otherwise plain order.
     const int xcd_order = (tiles % 8 == 0) ? 1 : 0;
     const size_t lds = (size_t)2 * GemmSlice<FMT>::XTILE * sizeof(uint16_t);
-    hipLaunchKernelGGL((gemm_kernel<FMT>), dim3((unsigned)tiles), dim3(kGemmThreads), lds, st, a.codes, a.scales,
-                       a.gscale, a.x, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
+    // NVFP4 rows of an odd multiple of 16 elements: 8-byte rows (ROW8)
+    if (FMT == kNVFP4 && a.k % 32 != 0)
+        hipLaunchKernelGGL((gemm_kernel<FMT, FMT == kNVFP4>), dim3((unsigned)tiles), dim3(kGemmThreads), lds, st,
+                           a.codes, a.scales, a.gscale, a.x, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
+    else
+        hipLaunchKernelGGL((gemm_kernel<FMT, false>), dim3((unsigned)tiles), dim3(kGemmThreads), lds, st, a.codes,
+                           a.scales, a.gscale, a.x, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
 }
 
 bool launch_gemm(const GemmArgs& a, hipStream_t st) {

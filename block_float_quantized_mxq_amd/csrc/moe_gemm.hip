@@ -86,7 +86,7 @@ constexpr int kMoeGemmWaves = 8;    // waves per workgroup (measured on MI355X: 
 // blocks of its row in registers -- blocks kb0 + 4j + g, j < MB -- loaded once
 // and used for every block of 16 pairs, so the expert's weights leave HBM
 // once per call.
-template <int FMT, int KS, int MB>
+template <int FMT, int KS, int MB, bool ROW8>
 __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
 
     const int64_t rowbytes = code_bytes_per_row(FMT, k);
     const int64_t sbytes = k / block_elems(FMT);
-    const int64_t nblk = k / 32;
+    const int64_t nblk = (k + 31) / 32;  // ROW8 (NVFP4, k an odd multiple of 16): the last block is half
     const int64_t kb0 = (int64_t)kp * MB * 4;
     const int64_t kb1 = kb0 + MB * 4 < nblk ? kb0 + MB * 4 : nblk;
     const int64_t rowt = (int64_t)blockIdx.x * ROWS + (int64_t)wr * 16;
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         const int64_t b = kb0 + 4 * j + g;
         const bool ok = b < kb1;
         valid |= (ok ? 1u : 0u) << j;
-        load_block<FMT>(crow, srow, ok ? b : 0, w[j]);
+        if constexpr (ROW8) load_wfrag<FMT, 32, true>(crow, srow, (ok ? b : 0) * 32, k, w[j]);
+        else load_block<FMT>(crow, srow, ok ? b : 0, w[j]);
     }
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
@@ -186,8 +187,11 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) v[s4] = u32x4g_t{0u, 0u, 0u, 0u};
             if (xlive && ((valid >> j) & 1u)) {
+                // ROW8: the last block is half; its staged row ends at k (no read past it)
+                const bool half = ROW8 && (kb0 + 4 * j + g) * 32 + 32 > k;
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) v[s4] = xp0[j * 16 + s4];
+                for (int s4 = 0; s4 < 4; ++s4)
+                    if (!(half && s4 >= 2)) v[s4] = xp0[j * 16 + s4];
             }
         };
         u32x4g_t vb[2][4];
@@ -252,9 +256,14 @@ static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const 
     constexpr int ROWS = kMoeGemmWaves / KS * 16;
     const int64_t tiles = (a.n + ROWS - 1) / ROWS;
     static_assert(kPairsPerBlock == 16, "moe_gemm_x_lds assumes blocks of 16 pairs");
-    hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB>), dim3((unsigned)tiles, (unsigned)a.experts),
-                       dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff,
-                       gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
+    if (FMT == kNVFP4 && a.k % 32 != 0)
+        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), dim3((unsigned)tiles, (unsigned)a.experts),
+                           dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale,
+                           goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
+    else
+        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, false>), dim3((unsigned)tiles, (unsigned)a.experts),
+                           dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale,
+                           goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
 // Register blocks per lane (MB) and k split (KS): the smallest capacity
@@ -267,7 +276,7 @@ static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t pairs = a.m * a.topk;
     int32_t* goff = a.workspace;
     int32_t* gperm = a.workspace + a.experts + 1;
-    const int64_t nblk = a.k / 32;
+    const int64_t nblk = (a.k + 31) / 32;
     static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
     static constexpr int kCand8[][2] = {{1, 4}, {2, 4}, {4, 4}, {8, 4}};
     int best_ks = 0, best_mb = 0;

@@ -181,7 +181,9 @@ mxq_status_t mxq_moe_gemv(mxq_format_t fmt, const uint8_t *codes, const uint8_t 
  *   x       bf16 [m][k]
  *   y       [m][n], fp32 (y_dtype MXQ_OUT_F32) or bf16 rounded to nearest even
  *           from the fp32 result (MXQ_OUT_BF16)
- *   m, n, k >= 1, < 2^31; k % 32 == 0 for every format
+ *   m, n, k >= 1, < 2^31; k a multiple of the block size (32 MX, 16 NVFP4)
+ * Up to 32 rows of X run on the matrix-unit GEMV (one B-operand column per
+ * row) when k % 32 == 0; everything else on 256 x 256 output tiles.
  */
 mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                       const uint16_t *x, void *y, mxq_out_t y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
@@ -290,8 +292,9 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  *   workspace      int32 [num_experts + 1 + m * topk], caller-owned, 4-byte
  *                  aligned: per-expert offsets, then the grouped pair order
  *   m 1 .. 2^24 / topk;  topk 1 .. MXQ_MAX_TOPK;  num_experts 1 .. 1024;
- *   n >= 1;  k a positive multiple of 32, at most 4088 (the inputs of 16 pairs
- *   are staged in 128 KiB of LDS; larger k gives MXQ_E_UNSUPPORTED)
+ *   n >= 1;  k a positive multiple of the block size (32 MX, 16 NVFP4), at
+ *   most 4088 (the inputs of 16 pairs are staged in 128 KiB of LDS; larger k
+ *   gives MXQ_E_UNSUPPORTED)
  * A pair whose id is outside [0, num_experts) gets a NaN output row.  Two
  * kernels run on `stream` (grouping, then the GEMM); the workspace must not be
  * shared by calls that overlap.

@@ -123,11 +123,11 @@ def test_shape_errors():
         assert moe(E=bad) == SHAPE and moe(n=bad) == SHAPE and moe(T=bad) == SHAPE and moe(topk=bad) == SHAPE
         assert gemm(m=bad) == SHAPE and gemm(n=bad) == SHAPE and gemm(k=bad) == SHAPE
         assert deq(rows=bad) == SHAPE and deq(k=bad) == SHAPE
-    # k must be a whole number of blocks: 32 for MX formats, 16 for NVFP4 (GEMM: 32 for all)
+    # k must be a whole number of blocks: 32 for MX formats, 16 for NVFP4 (the GEMMs too)
     assert gemv(fmt=1, k=48) == SHAPE and gemv(fmt=2, k=16) == SHAPE
     assert gemv(fmt=3, g=A, k=40) == SHAPE
     assert moe(fmt=1, k=16) == SHAPE and deq(fmt=2, k=80) == SHAPE
-    assert gemm(fmt=3, g=A, k=48) == SHAPE
+    assert gemm(fmt=3, g=A, k=40) == SHAPE and gemm(fmt=1, k=48) == SHAPE and gemm(fmt=2, k=16) == SHAPE
     for bad in (0, -1):
         assert route(T=bad) == SHAPE and route(E=bad) == SHAPE and route(topk=bad) == SHAPE
         assert block(E=bad) == SHAPE and block(hidden=bad) == SHAPE and block(dff=bad) == SHAPE
@@ -141,7 +141,7 @@ def test_shape_errors():
     for bad in (0, -1):
         for arg in ("E", "m", "n", "k", "topk"):
             assert mgemm(**{arg: bad}) == SHAPE, arg
-    assert mgemm(k=48) == SHAPE and mgemm(fmt=3, g=A, k=16) == SHAPE  # whole 32-element blocks
+    assert mgemm(k=48) == SHAPE and mgemm(fmt=3, g=A, k=24) == SHAPE  # whole blocks
     assert mgemm(ydt=2) == FORMAT
     for bad in (0, -1):
         assert quant(rows=bad) == SHAPE and quant(k=bad) == SHAPE
@@ -230,6 +230,7 @@ def test_device_error_without_gpu():
     assert gemv() == DEVICE and moe() == DEVICE and gemm() == DEVICE and deq() == DEVICE
     assert route() == DEVICE and block() == DEVICE and mgemm() == DEVICE
     assert mgemm(m=(1 << 24) // 8, topk=8, E=1024, k=4064) == DEVICE  # largest accepted sizes
+    assert gemm(fmt=3, g=A, k=48) == DEVICE and mgemm(fmt=3, g=A, k=48) == DEVICE  # NVFP4 half-block rows
     assert quant() == DEVICE and quant(fmt=3, g=A, k=48) == DEVICE and quant(rows=1 << 20, k=1 << 16) == DEVICE
     assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
     # the largest workspace every admitted call needs (8 tokens x 16 slots x 2048 columns x 10 bytes) fits the array

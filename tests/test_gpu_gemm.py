@@ -48,6 +48,22 @@ def test_bf16_output_is_rne_of_fp32(fmt, m):
     assert torch.equal(y16.cpu().view(torch.int16), rne.view(torch.int16))
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 7, 16), (40, 200, 48), (300, 129, 80), (17, 64, 1040), (260, 300, 5136)])
+def test_nvfp4_rows_of_an_odd_number_of_blocks(m, n, k):
+    """NVFP4 with k an odd multiple of 16: 8-byte rows whose last 32-element fragment
+    holds one block (the matrix-unit GEMV needs whole 32-element blocks, so every m
+    runs on the tiles); every output, and bf16 = RNE(fp32)."""
+    c = small_case(3, m, n, k, m + n + k)
+    say("gemm nvfp4 half-block rows", m, n, k)
+    args = (3, dev_u8(c["codes"]), dev_u8(c["scales"]), dev_bf16(c["x"]), dev_f32(c["g"]))
+    y32 = mxq.gemm(*args, out_dtype=torch.float32)
+    y16 = mxq.gemm(*args, out_dtype=torch.bfloat16)
+    Y_ref, A_ref = oracle.gemm_rows(3, c["codes"], c["scales"], c["g"], c["x"], np.arange(m), n, k)
+    assert_within(host(y32), Y_ref, A_ref, f"gemm nvfp4 {m}x{n}x{k}")
+    torch.cuda.synchronize()
+    assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
+
+
 def test_gemm_rows_match_gemv():
     c = small_case(1, 9, 640, 1024, 12)
     say("gemm row == gemv")

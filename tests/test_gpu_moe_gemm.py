@@ -54,6 +54,15 @@ def test_all_outputs(fmt, E, n, k, m, topk, per):
     check(c, f"moe gemm {FMT_NAMES[fmt]} E={E} n={n} k={k} m={m} topk={topk} per_slot={per}")
 
 
+@pytest.mark.parametrize("E,n,k,m,topk,per", [(8, 100, 48, 30, 2, 0), (16, 129, 784, 40, 4, 1),
+                                               (4, 64, 2064, 17, 2, 0)])
+def test_nvfp4_rows_of_an_odd_number_of_blocks(E, n, k, m, topk, per):
+    """NVFP4 with k an odd multiple of 16: the lane holding the last block holds half a
+    block (8-byte code rows, one scale), every output checked."""
+    c = case(3, E, n, k, m, topk, E + n + k + m, per)
+    check(c, f"moe gemm nvfp4 half-block rows E={E} n={n} k={k} m={m} topk={topk} per_slot={per}")
+
+
 @pytest.mark.parametrize("fmt", [1, 3])
 def test_one_expert_takes_several_row_tiles(fmt):
     """Every token routes to experts 0..3: expert 0 gets 600 pairs (three 256-row
