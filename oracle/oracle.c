@@ -267,8 +267,10 @@ void orc_gemm_rows(int fmt, const uint8_t *codes, const uint8_t *scales, const f
  *            [p - delta_j, p + delta_j] (rounding is monotone: the two ends),
  *   amb_y[t][i] = sum_s |w| sum_j |W_dn[e_s][i][j]| dev_j.
  * This is a bound on the acceptance test, not part of the block's result.
- * parity of amb_y unpinned beyond its invariants (zero when delta is zero,
- * covers every rounding inside the interval). */
+ * Pinned by its invariants (zero when delta is zero; it covers a fp32
+ * implementation's own rounding) and by brute force: on a small block every
+ * combination of legitimate bf16 values is enumerated, and amb_y covers the
+ * largest move of every output and equals it where all moves align. */
 
 /* k largest of l[0..E) (ties: lower index first), in that order. */
 void orc_moe_route(const float *logits, int64_t tokens, int64_t experts, int64_t topk, int renorm,

@@ -442,6 +442,66 @@ def check_block_rounding_bound():
             assert np.median(amb / a) < 1e-7
 
 
+def check_block_rounding_bound_bruteforce(seed=43, p_rel=2.0 ** -10):
+    """amb_y against brute force.  A one-expert MXFP4 block (hidden 32, expert width
+    32, one token, weight w) whose gate/up values are exact in fp32 (h_rel = h_abs =
+    0), so an activation's legitimate values are the bf16 roundings of every value
+    within p_rel * |p| of its fp32 product p.  From pinned pieces (the oracle's MoE
+    GEMV, numpy's fp32 SwiGLU, torch's bf16 rounding) the test lists each
+    activation's candidates, enumerates every combination of them, and takes the
+    largest |y(combination) - y| per output: amb_y must cover it everywhere and equal
+    it on output 0, whose down row is built so that every activation's other
+    candidate moves y the same way."""
+    rng = np.random.default_rng(seed)
+    H = dff = 32
+    gc = rng.integers(0, 256, size=(1, 2 * dff, H // 2), dtype=np.uint8)
+    gs = rng.integers(124, 127, size=(1, 2 * dff, 1), dtype=np.uint8)
+    # x: small integers, so that every gate/up sum is an fp32 number (exact in any order)
+    f = rng.integers(-3, 4, size=(1, H)).astype(np.float32)
+    x = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    ids = np.zeros((1, 1), dtype=np.int32)
+    w = np.array([[0.75]], dtype=np.float32)
+    h, _ = oracle.moe_gemv(MXFP4, gc, gs, None, ids, x, 0, 1, 2 * dff, H)
+    h32 = h[0, 0].astype(np.float32)
+    assert (h32.astype(np.float64) == h[0, 0]).all()              # premise: gate/up exact in fp32
+    g, u = h32[:dff].astype(np.float64), h32[dff:]
+    p = ((g / (1.0 + np.exp(-g))).astype(np.float32) * u).astype(np.float64)   # fp32 SwiGLU product
+    rne = lambda v: torch.from_numpy(np.asarray(v, dtype=np.float64)).to(torch.bfloat16).double().numpy()
+    a = rne(p)
+    lo, hi = rne(p - p_rel * np.abs(p)), rne(p + p_rel * np.abs(p))
+    cands = []
+    for j in range(dff):
+        # every bf16 value from lo to hi (rounding is monotone): step through the bf16 grid
+        c, v = [], torch.tensor([lo[j]], dtype=torch.float64).to(torch.bfloat16)
+        while float(v) <= hi[j]:
+            c.append(float(v))
+            v = torch.nextafter(v, torch.tensor([np.inf], dtype=torch.bfloat16))
+        cands.append(c)
+    unsure = [j for j in range(dff) if len(cands[j]) > 1]
+    assert 6 <= len(unsure) <= 16, len(unsure)                     # premise: enough choices to matter
+    # down bank: row 0 = the sign of each unsure activation's other candidate, random rows otherwise
+    dcodes = rng.integers(0, 256, size=(1, H, dff // 2), dtype=np.uint8)
+    dcodes[0, 0, :] = 0
+    for j in unsure:
+        other = max(cands[j], key=lambda v: abs(v - a[j]))
+        code = 0x2 if other > a[j] else 0xA                        # E2M1 +1 / -1
+        dcodes[0, 0, j // 2] |= code << (4 * (j % 2))
+    dscales = np.full((1, H, 1), 127, dtype=np.uint8)
+    Wdn = oracle.dequant(MXFP4, dcodes[0], dscales[0], None, H, dff).astype(np.float64)
+    y, _, amb = oracle.moe_block(MXFP4, gc, gs, None, dcodes, dscales, None, ids, w, x, 1, H, dff,
+                                 rounding_tol=(0.0, 0.0, p_rel))
+    ya = float(w[0, 0]) * (Wdn @ a)                               # fp64, its own summation order
+    assert (np.abs(y[0] - ya) <= 1e-14 * float(w[0, 0]) * (np.abs(Wdn) @ np.abs(a))).all()
+    # every combination of candidates
+    combos = np.array(np.meshgrid(*[cands[j] for j in unsure], indexing="ij")).reshape(len(unsure), -1).T
+    A = np.tile(a, (combos.shape[0], 1))
+    A[:, unsure] = combos
+    ys = float(w[0, 0]) * (A @ Wdn.T)
+    worst = np.abs(ys - y[0]).max(axis=0)
+    assert (amb[0] >= worst * (1 - 1e-12)).all(), (amb[0], worst)
+    assert abs(amb[0, 0] - worst[0]) <= 1e-12 * worst[0] and worst[0] > 0, (amb[0, 0], worst[0])
+
+
 # ---- block-float quantizer ---------------------------------------------------------------
 # An independent reference: element values from the stored E2M1 table and torch's E4M3
 # decoder, the nearest value found by exhaustive search (ties: even code), the MX scale
@@ -682,7 +742,8 @@ def all_checks():
                 (f"gemm_rows_{f}", lambda f=f: check_gemm_rows_bruteforce(f)),
                 (f"moe_block_{f}", lambda f=f: check_moe_block(f))]
     out += [("route", check_route), ("silu", check_silu), ("round_bf16", check_round_bf16),
-            ("swiglu_tie", check_swiglu_tie), ("block_rounding_bound", check_block_rounding_bound)]
+            ("swiglu_tie", check_swiglu_tie), ("block_rounding_bound", check_block_rounding_bound),
+            ("block_rounding_bound_bruteforce", check_block_rounding_bound_bruteforce)]
     out += [(f"quantize_nearest_{f}", lambda f=f: check_quantize_nearest(f)) for f in FMTS]
     out += [("quantize_scale_closed_form", check_quantize_scale_closed_form),
             ("quantize_roundtrip_mxfp4", lambda: check_quantize_roundtrip(MXFP4)),

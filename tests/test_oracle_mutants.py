@@ -48,6 +48,9 @@ MUTANTS = {
     "bf16_round_spacing": ("int q = (e < emin ? emin : e) - 8;", "int q = (e < emin ? emin : e) - 9;"),
     "block_silu_on_up": ("(double)(float)orc_silu(g32);", "(double)(float)orc_silu(u32);"),
     "block_weight_dropped": ("acc += ws * part;", "acc += part;"),
+    "amb_one_side": ("dev[s * dff + j] = lo > hi ? lo : hi;", "dev[s * dff + j] = lo;"),
+    "amb_half_interval": ("p_rel * fabs(p);", "0.5 * p_rel * fabs(p);"),
+    "amb_weight_dropped": ("bacc += fabs(ws) * bpart;", "bacc += bpart;"),
     "block_no_bf16": ("a[s * dff + j] = orc_round_bf16(p);", "a[s * dff + j] = p;"),
     "block_fp64_swiglu": ("const double p = (double)(float)(s32 * u32);", "const double p = orc_silu(g32) * u32;"),
     "requant_tile_col": ("tile_scales[(r / bn) * tcols + col / bk]", "tile_scales[(r / bn) * tcols + col / bn]"),
