@@ -60,12 +60,13 @@ def lib() -> ctypes.CDLL:
         L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
         L.mxq_moe_block_noalloc.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+        L.mxq_moe_block_routed.argtypes = [I, P, P, P, P, P, P, P, I, P, P, P, P, P, I64, I64, I64, I64, I64, P]
         L.mxq_moe_gemm.argtypes = [I, P, P, P, P, P, I, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_requant_fp8.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
         L.mxq_stream_read.argtypes = [P, I64, I, P, I64, P]
         for f in (L.mxq_gemv, L.mxq_gemv_config, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
-                  L.mxq_moe_block_noalloc, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8, L.mxq_stream_read):
+                  L.mxq_moe_block_noalloc, L.mxq_moe_block_routed, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8, L.mxq_stream_read):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
         L.mxq_status_string.restype = ctypes.c_char_p
@@ -268,6 +269,58 @@ def moe_block(fmt, gu_codes, gu_scales, dn_codes, dn_scales, expert_ids, weights
                                _ptr(h), _ptr(out), experts, hidden, dff, tokens, topk, _stream(stream)),
            "mxq_moe_block")
     return out
+
+
+def moe_block_routed(fmt, gu_codes, gu_scales, dn_codes, dn_scales, logits, topk, x, renorm=False,
+                     gu_global_scale=None, dn_global_scale=None, h=None, out=None, ids=None, weights=None,
+                     stream=None):
+    """MoE decode block that routes in place from float32 router logits [tokens, experts] (the selection
+    and weights of moe_route, bit for bit) -> (float32 y [tokens, hidden], int32 ids [tokens, topk],
+    float32 weights [tokens, topk]).  h as in moe_block (allocated when None)."""
+    gu_codes = _dev(gu_codes, torch.uint8, "gu_codes")
+    gu_scales = _dev(gu_scales, torch.uint8, "gu_scales")
+    dn_codes = _dev(dn_codes, torch.uint8, "dn_codes")
+    dn_scales = _dev(dn_scales, torch.uint8, "dn_scales")
+    logits = _dev(logits, torch.float32, "logits")
+    x = _dev(x, torch.bfloat16, "x")
+    gu_global_scale = _dev(gu_global_scale, torch.float32, "gu_global_scale")
+    dn_global_scale = _dev(dn_global_scale, torch.float32, "dn_global_scale")
+    experts, two_dff = gu_codes.shape[0], gu_codes.shape[1]
+    hidden = _check_weight(fmt, gu_codes, gu_scales, gu_global_scale, experts=experts)
+    dff = _check_weight(fmt, dn_codes, dn_scales, dn_global_scale, experts=experts)
+    if two_dff != 2 * dff or tuple(dn_codes.shape[:2]) != (experts, hidden):
+        raise ValueError(f"gate/up bank {tuple(gu_codes.shape)} and down bank {tuple(dn_codes.shape)} disagree")
+    if logits.dim() != 2 or logits.shape[1] != experts:
+        raise ValueError(f"logits must be [tokens, {experts}], got {tuple(logits.shape)}")
+    tokens = logits.shape[0]
+    if tuple(x.shape) != (tokens, hidden):
+        raise ValueError(f"x must have shape {(tokens, hidden)}, got {tuple(x.shape)}")
+    dev = gu_codes.device
+    need = moe_block_workspace_elems(tokens, topk, dff)
+    if h is None:
+        h = torch.empty(need, dtype=torch.float32, device=dev)
+    h = _dev(h, torch.float32, "h")
+    if h.numel() < need:
+        raise ValueError(f"h must hold moe_block_workspace_elems(tokens, topk, dff) = {need} elements")
+    if out is None:
+        out = torch.empty((tokens, hidden), dtype=torch.float32, device=dev)
+    if ids is None:
+        ids = torch.empty((tokens, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((tokens, topk), dtype=torch.float32, device=dev)
+    out = _dev(out, torch.float32, "out")
+    ids = _dev(ids, torch.int32, "ids")
+    weights = _dev(weights, torch.float32, "weights")
+    if out.numel() != tokens * hidden:
+        raise ValueError("out must hold tokens * hidden elements")
+    if ids.numel() != tokens * topk or weights.numel() != tokens * topk:
+        raise ValueError("ids and weights must hold tokens * topk elements")
+    _check(lib().mxq_moe_block_routed(fmt, _ptr(gu_codes), _ptr(gu_scales), _ptr(gu_global_scale),
+                                      _ptr(dn_codes), _ptr(dn_scales), _ptr(dn_global_scale), _ptr(logits),
+                                      1 if renorm else 0, _ptr(ids), _ptr(weights), _ptr(x), _ptr(h), _ptr(out),
+                                      experts, hidden, dff, tokens, topk, _stream(stream)),
+           "mxq_moe_block_routed")
+    return out, ids, weights
 
 
 def gemm(fmt, codes, scales, x, global_scale=None, out_dtype=torch.bfloat16, out=None, stream=None):

@@ -92,7 +92,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 8; }
+MXQ_API int mxq_abi_version(void) { return 9; }
 
 MXQ_API mxq_status_t mxq_gemv(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -326,17 +326,25 @@ mxq_status_t check_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu
 }
 
 // The block's two kernels on validated arguments, with the workspace at h.
+// With logits set, the gate/up kernel routes in place and writes the ids and
+// weights (expert_ids / weights are then its outputs).
 mxq_status_t run_moe_block(int fmt, const uint8_t* gu_codes, const uint8_t* gu_scales, const float* gu_gscale,
                            const uint8_t* dn_codes, const uint8_t* dn_scales, const float* dn_gscale,
                            const int32_t* expert_ids, const float* weights, const uint16_t* x, float* h, float* y,
                            int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens, int64_t topk, int cus,
-                           void* stream) {
+                           void* stream, const float* logits = nullptr, int renorm = 0) {
     mxq_status_t st;
     // workspace: gate/up outputs, then the bf16 activations
     uint16_t* act = reinterpret_cast<uint16_t*>(h + tokens * topk * 2 * dff);
     mxq::MoeArgs gu{fmt, gu_codes, gu_scales, gu_gscale, expert_ids, x, 0, h, num_experts, 2 * dff, hidden,
                     tokens, topk, cus};
     gu.act = act;
+    if (logits) {
+        gu.logits = logits;
+        gu.renorm = renorm ? 1 : 0;
+        gu.ids_out = const_cast<int32_t*>(expert_ids);
+        gu.weights_out = const_cast<float*>(weights);
+    }
     if ((st = launched(mxq::launch_moe(gu, as_stream(stream)))) != MXQ_OK) return st;
     const mxq::MoeBlockArgs dn{fmt, dn_codes, dn_scales, dn_gscale, expert_ids, weights, act, y, num_experts, hidden,
                                dff, tokens, topk};
@@ -357,6 +365,25 @@ MXQ_API mxq_status_t mxq_moe_block(mxq_format_t fmt, const uint8_t* gu_codes, co
     if ((st = check_device(&cus)) != MXQ_OK) return st;
     return run_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids, weights, x, h,
                          y, num_experts, hidden, dff, tokens, topk, cus, stream);
+}
+
+MXQ_API mxq_status_t mxq_moe_block_routed(mxq_format_t fmt, const uint8_t* gu_codes, const uint8_t* gu_scales,
+                                          const float* gu_gscale, const uint8_t* dn_codes, const uint8_t* dn_scales,
+                                          const float* dn_gscale, const float* logits, int renorm,
+                                          int32_t* expert_ids, float* weights, const uint16_t* x, float* h, float* y,
+                                          int64_t num_experts, int64_t hidden, int64_t dff, int64_t tokens,
+                                          int64_t topk, void* stream) {
+    mxq_status_t st = check_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids,
+                                      weights, x, h, true, y, num_experts, hidden, dff, tokens, topk);
+    if (st != MXQ_OK) return st;
+    if (!logits) return MXQ_E_NULLPTR;
+    if (topk > num_experts) return MXQ_E_SHAPE;
+    if (!aligned(logits, 4)) return MXQ_E_ALIGN;
+    if (num_experts > 1024) return MXQ_E_UNSUPPORTED;
+    int cus = 0;
+    if ((st = check_device(&cus)) != MXQ_OK) return st;
+    return run_moe_block(fmt, gu_codes, gu_scales, gu_gscale, dn_codes, dn_scales, dn_gscale, expert_ids, weights, x, h,
+                         y, num_experts, hidden, dff, tokens, topk, cus, stream, logits, renorm);
 }
 
 MXQ_API mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t* gu_codes, const uint8_t* gu_scales,

@@ -62,6 +62,13 @@ struct MoeArgs {
     // non-null: the rows are a SwiGLU layer's gate rows then up rows (n even),
     // and position q also gets bf16(silu(gate) * up) at act + q n/2
     uint16_t* act = nullptr;
+    // non-null (with act): the kernel routes in place from router logits
+    // [tokens][experts] and writes the ids and weights it used to ids_out and
+    // weights_out (ids is then not read)
+    const float* logits = nullptr;
+    int renorm = 0;
+    int32_t* ids_out = nullptr;
+    float* weights_out = nullptr;
 };
 
 struct DequantArgs {

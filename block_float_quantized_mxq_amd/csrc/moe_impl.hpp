@@ -15,6 +15,7 @@
 #pragma once
 
 #include "kernels.hpp"
+#include "moe_route.hpp"
 #include "rows_core.hpp"
 
 namespace mxq {
@@ -91,10 +92,15 @@ __device__ __forceinline__ void moe_round(const uint8_t* codes, const uint8_t* s
 // PAIR: the rows are a SwiGLU layer's gate rows then up rows, and position q
 // also gets its activations bf16(silu(gate) * up) at act + q n/2 (a position
 // with an invalid id gets NaN outputs and no activations).
+// RNS > 0: the kernel routes in place (moe_route.hpp, RNS logits per lane):
+// wave w of every workgroup routes tokens w, w + 4, ... into LDS, and
+// workgroup (0, 0) also writes the ids and weights to ids_out / weights_out.
+// Every workgroup computes the same routing, so they all agree on it; this
+// spares the routing launch.
 // At least 3 waves per SIMD: the two-vector loops sit just under the 170
 // registers that allow 3 (a few more registers would halve the waves in
 // flight: MI355X, 30B-A3B gate/up with SwiGLU, 2 tokens 8 -> 12 us).
-template <int FMT, int CB, int G, int S, int R, bool XL, int RC, bool PAIR>
+template <int FMT, int CB, int G, int S, int R, bool XL, int RC, bool PAIR, int RNS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void moe_kernel(const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gscale,
@@ -102,15 +108,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                                                        const uint16_t* __restrict__ x, int x_per_slot,
                                                        float* __restrict__ y, uint16_t* __restrict__ act,
                                                        int64_t experts, int64_t n, int64_t k, int pairs,
-                                                       int64_t topk) {
+                                                       int64_t topk, const float* __restrict__ logits, int renorm,
+                                                       int32_t* __restrict__ ids_out, float* __restrict__ weights_out) {
     using T = RowTile<G, S, R>;
     __shared__ float red[S > 1 ? S * T::ROWSETS * R * 8 : 1];
+    __shared__ int32_t rids[RNS > 0 ? kMaxPairs : 1];
+    __shared__ float rwts[RNS > 0 ? kMaxPairs : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
     const int p = blockIdx.y;
     const int64_t row0 = (int64_t)blockIdx.x * T::ROWS;
     const int wl = threadIdx.x & 63;
-    const int v0 = wl < pairs ? ids[wl] : -1;
-    const int v1 = wl + 64 < pairs ? ids[wl + 64] : -1;
+    int v0, v1;
+    if constexpr (RNS > 0) {
+        const int tokens = pairs / (int)topk;
+        for (int t = threadIdx.x >> 6; t < tokens; t += kThreads / 64)
+            route_wave<RNS>(logits + (int64_t)t * experts, (int)experts, (int)topk, renorm, rids + t * topk,
+                            rwts + t * topk);
+        __syncthreads();
+        if (blockIdx.x == 0 && blockIdx.y == 0)
+            for (int i = threadIdx.x; i < pairs; i += kThreads) {
+                ids_out[i] = rids[i];
+                weights_out[i] = rwts[i];
+            }
+        v0 = wl < pairs ? rids[wl] : -1;
+        v1 = wl + 64 < pairs ? rids[wl + 64] : -1;
+    } else {
+        v0 = wl < pairs ? ids[wl] : -1;
+        v1 = wl + 64 < pairs ? ids[wl + 64] : -1;
+    }
     const int e = __shfl(p < 64 ? v0 : v1, p & 63, 64);
     if (e < 0 || (int64_t)e >= experts) {
         for (int t = threadIdx.x; t < T::ROWS; t += kThreads)
@@ -163,26 +188,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 }
 
-template <int FMT, int CB, int G, int S, int R, int RC, bool PAIR>
+template <int FMT, int CB, int G, int S, int R, int RC, bool PAIR, int RNS>
 static void launch_moe_rc(const MoeArgs& a, hipStream_t st) {
     using T = RowTile<G, S, R>;
     const int64_t tiles = (a.n + T::ROWS - 1) / T::ROWS;
     const int pairs = (int)(a.tokens * a.topk);
     const int64_t lds = x_lds_bytes<FMT, CB>(a.k, RC);
     if (lds <= kMoeMaxXLds)
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true, RC, PAIR>), dim3((unsigned)tiles, (unsigned)pairs),
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, true, RC, PAIR, RNS>), dim3((unsigned)tiles, (unsigned)pairs),
                            dim3(kThreads), (size_t)lds, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y,
-                           a.act, a.experts, a.n, a.k, pairs, a.topk);
+                           a.act, a.experts, a.n, a.k, pairs, a.topk, a.logits, a.renorm, a.ids_out, a.weights_out);
     else
-        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false, RC, PAIR>), dim3((unsigned)tiles, (unsigned)pairs),
+        hipLaunchKernelGGL((moe_kernel<FMT, CB, G, S, R, false, RC, PAIR, RNS>), dim3((unsigned)tiles, (unsigned)pairs),
                            dim3(kThreads), 0, st, a.codes, a.scales, a.gscale, a.ids, a.x, a.x_per_slot, a.y, a.act,
-                           a.experts, a.n, a.k, pairs, a.topk);
+                           a.experts, a.n, a.k, pairs, a.topk, a.logits, a.renorm, a.ids_out, a.weights_out);
 }
 
-template <int FMT, int CB, int G, int S, int R, bool PAIR = false>
+template <int FMT, int CB, int G, int S, int R, bool PAIR = false, int RNS = 0>
 static void launch_moe_inst(const MoeArgs& a, hipStream_t st) {
-    if (moe_round_cap(a.tokens) == 1) launch_moe_rc<FMT, CB, G, S, R, 1, PAIR>(a, st);
-    else launch_moe_rc<FMT, CB, G, S, R, 2, PAIR>(a, st);
+    if (moe_round_cap(a.tokens) == 1) launch_moe_rc<FMT, CB, G, S, R, 1, PAIR, RNS>(a, st);
+    else launch_moe_rc<FMT, CB, G, S, R, 2, PAIR, RNS>(a, st);
+}
+
+// The SwiGLU (paired-row) form, routing in place when a.logits is set: two
+// logits per lane up to 128 experts, else 16 (1024 experts).
+template <int FMT, int CB, int G>
+static void launch_moe_pair(const MoeArgs& a, hipStream_t st) {
+    if (!a.logits) launch_moe_inst<FMT, CB, G, 1, 2, true, 0>(a, st);
+    else if (a.experts <= 128) launch_moe_inst<FMT, CB, G, 1, 2, true, 2>(a, st);
+    else launch_moe_inst<FMT, CB, G, 1, 2, true, kRouteSlots>(a, st);
 }
 
 // Tile shape: lanes per row (g), k split (s), rows per lane (r), from the
@@ -196,11 +230,13 @@ static bool launch_moe_cb(const MoeArgs& a, hipStream_t st) {
     if (a.act) {
         // SwiGLU pairs: two rows per lane, the lanes per row of the plain shapes
         if (a.n % 2) return false;
-        if (nchunks >= 64 && a.tokens <= 4) launch_moe_inst<FMT, CB, 16, 1, 2, true>(a, st);
-        else if (nchunks >= 8) launch_moe_inst<FMT, CB, 8, 1, 2, true>(a, st);
-        else launch_moe_inst<FMT, CB, 4, 1, 2, true>(a, st);
+        if (a.logits && a.experts > kRouteMaxExperts) return false;
+        if (nchunks >= 64 && a.tokens <= 4) launch_moe_pair<FMT, CB, 16>(a, st);
+        else if (nchunks >= 8) launch_moe_pair<FMT, CB, 8>(a, st);
+        else launch_moe_pair<FMT, CB, 4>(a, st);
         return true;
     }
+    if (a.logits) return false;  // in-place routing only in the SwiGLU form
     int g = 16, sp = 1, r = 2;
     if (nchunks < 64) {
         r = 1;

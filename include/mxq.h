@@ -254,6 +254,25 @@ mxq_status_t mxq_moe_block(mxq_format_t fmt, const uint8_t *gu_codes, const uint
                            void *stream);
 
 /*
+ * MoE decode block with the routing of mxq_moe_route done in place: the
+ * gate/up kernel selects each token's experts and weights from its router
+ * logits (the same selection and the same fp32 weights, bit for bit, as
+ * mxq_moe_route), writes them to expert_ids and weights, and the block then
+ * proceeds as mxq_moe_block.  One launch fewer than mxq_moe_route followed by
+ * mxq_moe_block.
+ *   logits      fp32 [tokens][num_experts], num_experts 1 .. 1024, no NaN
+ *   renorm      nonzero: weights divided by the sum of the selected ones
+ *   expert_ids  int32 [tokens][topk] out;  weights fp32 [tokens][topk] out
+ *   topk        at most num_experts (else MXQ_E_SHAPE)
+ * Every other argument, limit and error as mxq_moe_block.
+ */
+mxq_status_t mxq_moe_block_routed(mxq_format_t fmt, const uint8_t *gu_codes, const uint8_t *gu_scales,
+                                  const float *gu_gscale, const uint8_t *dn_codes, const uint8_t *dn_scales,
+                                  const float *dn_gscale, const float *logits, int renorm, int32_t *expert_ids,
+                                  float *weights, const uint16_t *x, float *h, float *y, int64_t num_experts,
+                                  int64_t hidden, int64_t dff, int64_t tokens, int64_t topk, void *stream);
+
+/*
  * Allocation-free MoE decode block, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same computation, kernels and arguments as
@@ -368,7 +387,7 @@ mxq_status_t mxq_stream_read(const void *data, int64_t bytes, int layout, uint32
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 8 (7 with the MoE block workspace grown to hold the activations). */
+/* ABI version of this header: 9 (mxq_moe_block_routed added to 8). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

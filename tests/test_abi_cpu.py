@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["mxq_gemv", "mxq_gemv_config", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
-         "mxq_moe_block_noalloc", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_stream_read",
+         "mxq_moe_block_noalloc", "mxq_moe_block_routed", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_stream_read",
          "mxq_status_string",
          "mxq_abi_version"])
 
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 8
+    assert lib.mxq_abi_version() == 9
 
 
 def test_status_strings():
@@ -78,6 +78,12 @@ def block_na(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=Non
                                            E, hidden, dff, T, topk, None)
 
 
+def block_rt(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=None, logits=A, renorm=0, ids=A, w=A,
+             x=A, h=A, y=A, E=4, hidden=64, dff=64, T=1, topk=2):
+    return mxq.lib().mxq_moe_block_routed(fmt, codes, scales, g, dn_codes, dn_scales, dn_g, logits, renorm, ids, w,
+                                          x, h, y, E, hidden, dff, T, topk, None)
+
+
 def mgemm(fmt=1, codes=A, scales=A, g=None, ids=A, x=A, per=0, y=A, ydt=0, ws=A, E=4, m=3, n=8, k=64, topk=2):
     return mxq.lib().mxq_moe_gemm(fmt, codes, scales, g, ids, x, per, y, ydt, ws, E, m, n, k, topk, None)
 
@@ -86,7 +92,7 @@ def quant(fmt=1, x=A, g=None, codes=A, scales=A, rows=4, k=64):
     return mxq.lib().mxq_quantize(fmt, x, g, codes, scales, rows, k, None)
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, block_na, mgemm, quant])
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, block_na, block_rt, mgemm, quant])
 def test_format_errors(call):
     assert call(fmt=0) == FORMAT
     assert call(fmt=4) == FORMAT
@@ -95,7 +101,7 @@ def test_format_errors(call):
     assert call(fmt=2, g=A) == FORMAT
 
 
-@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, block_na, mgemm])
+@pytest.mark.parametrize("call", [gemv, moe, gemm, deq, block, block_na, block_rt, mgemm])
 def test_null_pointers(call):
     assert call(codes=None) == NULLPTR
     assert call(scales=None) == NULLPTR
@@ -111,6 +117,8 @@ def test_null_pointers_per_entry():
         assert block(**{arg: None}) == NULLPTR, arg
     for arg in ("dn_codes", "dn_scales", "ids", "w", "x", "y"):
         assert block_na(**{arg: None}) == NULLPTR, arg
+    for arg in ("dn_codes", "dn_scales", "logits", "ids", "w", "x", "h", "y"):
+        assert block_rt(**{arg: None}) == NULLPTR, arg
     for arg in ("ids", "x", "y", "ws"):
         assert mgemm(**{arg: None}) == NULLPTR, arg
     for arg in ("x", "codes", "scales"):
@@ -133,7 +141,11 @@ def test_shape_errors():
         assert block(E=bad) == SHAPE and block(hidden=bad) == SHAPE and block(dff=bad) == SHAPE
         assert block(T=bad) == SHAPE and block(topk=bad) == SHAPE
         assert block_na(E=bad) == SHAPE and block_na(dff=bad) == SHAPE and block_na(T=bad) == SHAPE
+    for bad in (0, -1):
+        for arg in ("E", "hidden", "dff", "T", "topk"):
+            assert block_rt(**{arg: bad}) == SHAPE, arg
     assert route(E=4, topk=5) == SHAPE                      # more picks than experts
+    assert block_rt(E=4, topk=5) == SHAPE and block_rt(dff=80) == SHAPE
     assert block(hidden=48) == SHAPE and block(dff=80) == SHAPE
     assert block(fmt=3, g=A, dn_g=A, dff=40) == SHAPE
     # the two banks of one block share the format: its per-tensor scales go with it
@@ -160,6 +172,9 @@ def test_alignment_errors():
     assert block(fmt=3, g=A, dn_g=A + 2) == ALIGN
     for arg, off in (("codes", 8), ("dn_codes", 4), ("x", 8), ("y", 2), ("ids", 2), ("w", 1)):
         assert block_na(**{arg: A + off}) == ALIGN, arg
+    for arg, off in (("codes", 8), ("dn_codes", 4), ("x", 8), ("h", 4), ("y", 2), ("ids", 2), ("w", 1),
+                     ("logits", 2)):
+        assert block_rt(**{arg: A + off}) == ALIGN, arg
     for arg, off in (("codes", 8), ("x", 8), ("y", 2), ("ids", 2), ("ws", 1)):
         assert mgemm(**{arg: A + off}) == ALIGN, arg
     assert quant(x=A + 8) == ALIGN and quant(codes=A + 8) == ALIGN and quant(fmt=3, g=A + 2, k=64) == ALIGN
@@ -176,6 +191,7 @@ def test_unsupported_sizes():
     assert block(topk=8, dff=4128) == UNSUPPORTED and block(topk=5, dff=4128) == UNSUPPORTED
     assert block(topk=4, dff=8224) == UNSUPPORTED and block(topk=2, dff=16416) == UNSUPPORTED
     assert block_na(T=9) == UNSUPPORTED and block_na(topk=8, dff=4128) == UNSUPPORTED
+    assert block_rt(T=9) == UNSUPPORTED and block_rt(E=1025) == UNSUPPORTED and block_rt(topk=8, dff=4128) == UNSUPPORTED
     assert mgemm(topk=17) == UNSUPPORTED and mgemm(E=1025) == UNSUPPORTED
     assert mgemm(m=(1 << 24) // 8 + 1, topk=8) == UNSUPPORTED and mgemm(n=1 << 31) == UNSUPPORTED
     assert mgemm(k=4096) == UNSUPPORTED  # 16 padded input rows must fit 128 KiB of LDS
@@ -235,6 +251,7 @@ def test_device_error_without_gpu():
     assert block(topk=8, dff=4096) == DEVICE and block(topk=2, dff=16384) == DEVICE  # LDS budget exactly met
     # the largest workspace every admitted call needs (8 tokens x 16 slots x 2048 columns x 10 bytes) fits the array
     assert block_na() == DEVICE and block_na(T=8, topk=16, dff=2048, E=16) == DEVICE
+    assert block_rt() == DEVICE and block_rt(E=1024, T=8, topk=16, dff=2048) == DEVICE
     assert gemv(fmt=3, g=A, k=48) == DEVICE  # NVFP4 rows of 24 bytes are valid too
     assert requant() == DEVICE and requant(n=1 << 20, k=1 << 16, bn=1, bk=32) == DEVICE
     assert gemv_cfg(dict()) == DEVICE and gemv_cfg(dict(path=4, mm_r=4, mm_s=2), batch=4) == DEVICE

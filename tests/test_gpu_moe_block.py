@@ -211,3 +211,45 @@ def test_route_then_block():
     y_ref, a_ref, amb = reference(c, ROUNDING_TOL_CONTRACT, ids_ref)
     # the routing weights differ by at most 1e-5 relative: another 1e-5 abs_y
     assert (np.abs(y - y_ref) <= 2e-5 * a_ref + amb + 1e-6).all()
+
+
+@pytest.mark.parametrize("fmt,experts,hidden,dff,topk,tokens,renorm", [
+    (1, 128, 2048, 768, 8, 1, True),   # the 30B-A3B-like block
+    (1, 128, 2048, 768, 8, 4, False),
+    (1, 128, 2048, 768, 8, 8, True),
+    (1, 40, 512, 256, 6, 3, True),     # fewer experts than lanes
+    (2, 300, 512, 160, 3, 8, True),    # MXFP8, experts past 128 (sixteen logits per lane)
+    (3, 1000, 256, 128, 16, 5, False), # NVFP4, 1000 experts, 16 slots
+    (1, 6, 256, 64, 6, 2, True),       # every expert selected
+])
+def test_routed_block_matches_route_then_block(fmt, experts, hidden, dff, topk, tokens, renorm):
+    """Routing in place in the gate/up kernel gives, bit for bit, the ids, weights, workspace and outputs of
+    mxq_moe_route followed by mxq_moe_block; the ids and weights also against the oracle's routing."""
+    c = synth.moe_block(tokens, seed=experts + topk, fmt=fmt, experts=experts, hidden=hidden, dff=dff, topk=topk)
+    logits = route_case(experts * 7 + tokens, tokens, experts)
+    gc, gs, gg = c["gu"]
+    dc, ds, dg = c["dn"]
+    say(f"routed block fmt={fmt} E={experts} H={hidden} dff={dff} topk={topk} T={tokens} renorm={renorm}")
+    banks = (dev_u8(gc), dev_u8(gs), dev_u8(dc), dev_u8(ds))
+    x = dev_bf16(c["x"])
+    lg = dev_f32(logits)
+    n_ws = mxq.moe_block_workspace_elems(tokens, topk, dff)
+    ws1 = torch.full((n_ws,), float("nan"), dtype=torch.float32, device="cuda:0")
+    ws2 = torch.full((n_ws,), float("nan"), dtype=torch.float32, device="cuda:0")
+    ids1, w1 = mxq.moe_route(lg, topk, renorm)
+    y1 = mxq.moe_block(fmt, *banks, ids1, w1, x, gu_global_scale=dev_f32(gg), dn_global_scale=dev_f32(dg), h=ws1)
+    y2, ids2, w2 = mxq.moe_block_routed(fmt, *banks, lg, topk, x, renorm=renorm, gu_global_scale=dev_f32(gg),
+                                        dn_global_scale=dev_f32(dg), h=ws2)
+    ids1, w1, ids2, w2 = host(ids1), host(w1), host(ids2), host(w2)
+    assert (ids1 == ids2).all(), (ids1, ids2)
+    assert (w1.view(np.uint32) == w2.view(np.uint32)).all(), (w1, w2)
+    h1, a1 = (host(v.float()) if v.dtype == torch.bfloat16 else host(v)
+              for v in mxq.moe_block_workspace_views(ws1, tokens, topk, dff))
+    h2, a2 = (host(v.float()) if v.dtype == torch.bfloat16 else host(v)
+              for v in mxq.moe_block_workspace_views(ws2, tokens, topk, dff))
+    assert (h1.view(np.uint32) == h2.view(np.uint32)).all()
+    assert (a1.view(np.uint32) == a2.view(np.uint32)).all()
+    assert (host(y1).view(np.uint32) == host(y2).view(np.uint32)).all()
+    ids_ref, w_ref = oracle.moe_route(logits, topk, renorm)
+    assert (ids2 == ids_ref).all()
+    assert (np.abs(w2 - w_ref) <= 1e-5 * w_ref + 1e-7).all()
