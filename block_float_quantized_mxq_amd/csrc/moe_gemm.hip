@@ -86,8 +86,10 @@ constexpr int kMoeGemmWaves = 8;    // waves per workgroup (measured on MI355X: 
 // blocks of its row in registers -- blocks kb0 + 4j + g, j < MB -- loaded once
 // and used for every block of 16 pairs, so the expert's weights leave HBM
 // once per call.
+// Two workgroups per CU (their LDS allows it) need at most 128 registers: 4
+// waves per SIMD for the 4-bit formats; E4M3 blocks take twice the registers.
 template <int FMT, int KS, int MB, bool ROW8>
-__global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
+__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kMXFP8 ? 2 : (FMT == kNVFP4 && MB == 8) ? 3 : 4))) void moe_gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
@@ -121,6 +123,38 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
     const uint8_t* srow = scales + (e * n + row) * sbytes;
     const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
 
+    // Gather of the input rows of a block of pairs into LDS: piece i of the
+    // block is row i / pieces, 16-byte column i % pieces; a round issues U
+    // pieces per thread (all of a 16 x 2048 block in one round), then stores them.
+    constexpr int U = 8, NT = NW * 64;
+    const int pieces = (int)(k / 8);
+    const int64_t xstride = mfma_x_stride(k);
+    u32x4g_t xv[U];
+    int dst[U];  // LDS 16-byte slot of each piece
+    auto gather_issue = [&](int i0, int total) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * NT < total ? i0 + u * NT : i0;
+            const int bi = i / pieces, ci = i - bi * pieces;
+            dst[u] = bi * (int)(xstride / 8) + ci;
+            xv[u] = *reinterpret_cast<const u32x4g_t*>(x + xrow_of[bi] * k + (int64_t)ci * 8);
+        }
+    };
+    auto gather_store = [&](int i0, int total) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * NT < total) reinterpret_cast<u32x4g_t*>(xlds)[dst[u]] = xv[u];
+    };
+    // The first block's rows are requested before the weights: the loads
+    // complete in order, so storing them to LDS then waits for them alone and
+    // the weights arrive while the workgroup stages and synchronises.
+    {
+        const int batch = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock);
+        if (tid < batch) xrow_of[tid] = gperm[c0 + tid] / xdiv;
+        __syncthreads();
+        if (tid < batch * pieces) gather_issue(tid, batch * pieces);
+    }
+
     // the lane's weight blocks: loaded once; blocks outside the k range read
     // a valid block and are zeroed (codes 0, unit scale)
     WFrag<FMT> w[MB];
@@ -133,6 +167,16 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         if constexpr (ROW8) load_wfrag<FMT, 32, true>(crow, srow, (ok ? b : 0) * 32, k, w[j]);
         else load_block<FMT>(crow, srow, ok ? b : 0, w[j]);
     }
+
+    // the rest of the first block's staging
+    {
+        const int total = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock) * pieces;
+        if (tid < total) gather_store(tid, total);
+        for (int i0 = tid + U * NT; i0 < total; i0 += U * NT) {
+            gather_issue(i0, total);
+            gather_store(i0, total);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
         const bool ok = (valid >> j) & 1u;
@@ -140,7 +184,6 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
         for (int d = 0; d < WFrag<FMT>::DW; ++d) w[j].w[d] = ok ? w[j].w[d] : 0u;
         w[j].s = ok ? w[j].s : (FMT == kNVFP4 ? 0x3838u : 127u);
     }
-    const int64_t xstride = mfma_x_stride(k);
     // MXFP8 weights with an E8M0 byte below kMx8Lift anywhere in the wave: their
     // lifted part runs as a second pass (block_operand.hpp); uniform over the wave
     bool lifted = false;
@@ -154,28 +197,15 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) void moe_gemm_kernel(
     for (int64_t t0 = 0; t0 < cnt; t0 += kPairsPerBlock) {
         const int batch = (int)(cnt - t0 < kPairsPerBlock ? cnt - t0 : kPairsPerBlock);
         const bool xlive = lr < batch;
-        __syncthreads();  // the previous block's LDS reads are done
-        if (tid < batch) xrow_of[tid] = gperm[c0 + t0 + tid] / xdiv;
-        __syncthreads();
-        // gather the input rows of this block's pairs: piece i of the block is
-        // row i / pieces, 16-byte column i % pieces; U pieces per thread in
-        // flight (all of a 16 x 2048 block in one round)
-        constexpr int U = 8, NT = NW * 64;
-        const int pieces = (int)(k / 8), total = batch * pieces;
-        for (int i0 = tid; i0 < total; i0 += U * NT) {
-            u32x4g_t v[U];
-            int bi[U], ci[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * NT < total ? i0 + u * NT : i0;
-                bi[u] = i / pieces;
-                ci[u] = i - bi[u] * pieces;
-                v[u] = *reinterpret_cast<const u32x4g_t*>(x + xrow_of[bi[u]] * k + (int64_t)ci[u] * 8);
+        if (t0 > 0) {
+            const int total = batch * pieces;
+            __syncthreads();  // the previous block's LDS reads are done
+            if (tid < batch) xrow_of[tid] = gperm[c0 + t0 + tid] / xdiv;
+            __syncthreads();
+            for (int i0 = tid; i0 < total; i0 += U * NT) {
+                gather_issue(i0, total);
+                gather_store(i0, total);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (i0 + u * NT < total)
-                    reinterpret_cast<u32x4g_t*>(xlds)[(int64_t)bi[u] * (xstride / 8) + ci[u]] = v[u];
         }
         __syncthreads();
 
