@@ -86,10 +86,17 @@ constexpr int kMoeGemmWaves = 8;    // waves per workgroup (measured on MI355X: 
 // blocks of its row in registers -- blocks kb0 + 4j + g, j < MB -- loaded once
 // and used for every block of 16 pairs, so the expert's weights leave HBM
 // once per call.
-// Two workgroups per CU (their LDS allows it) need at most 128 registers: 4
-// waves per SIMD for the 4-bit formats; E4M3 blocks take twice the registers.
+// XF: the first block's inputs are requested before the weights (below).
+// That keeps their registers live across the weight loads; the 4-bit formats
+// stay within the 128 registers of two workgroups per CU (their LDS allows
+// two) except NVFP4 with eight blocks per lane, which loads its weights first
+// (MI355X, 30B-A3B gate/up bank, 512 tokens: 176 us that way, 223 us with one
+// workgroup per CU).  E4M3 blocks take twice the registers either way.
+template <int FMT, int MB>
+constexpr bool moe_gemm_x_first() { return !(FMT == kNVFP4 && MB == 8); }
+
 template <int FMT, int KS, int MB, bool ROW8>
-__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kMXFP8 ? 2 : (FMT == kNVFP4 && MB == 8) ? 3 : 4))) void moe_gemm_kernel(
+__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kMXFP8 ? 2 : 4))) void moe_gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
@@ -145,10 +152,11 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
         for (int u = 0; u < U; ++u)
             if (i0 + u * NT < total) reinterpret_cast<u32x4g_t*>(xlds)[dst[u]] = xv[u];
     };
-    // The first block's rows are requested before the weights: the loads
+    // The first block's rows are requested before the weights (XF): the loads
     // complete in order, so storing them to LDS then waits for them alone and
     // the weights arrive while the workgroup stages and synchronises.
-    {
+    constexpr bool XF = moe_gemm_x_first<FMT, MB>();
+    if constexpr (XF) {
         const int batch = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock);
         if (tid < batch) xrow_of[tid] = gperm[c0 + tid] / xdiv;
         __syncthreads();
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
     }
 
     // the rest of the first block's staging
-    {
+    if constexpr (XF) {
         const int total = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock) * pieces;
         if (tid < total) gather_store(tid, total);
         for (int i0 = tid + U * NT; i0 < total; i0 += U * NT) {
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
     for (int64_t t0 = 0; t0 < cnt; t0 += kPairsPerBlock) {
         const int batch = (int)(cnt - t0 < kPairsPerBlock ? cnt - t0 : kPairsPerBlock);
         const bool xlive = lr < batch;
-        if (t0 > 0) {
+        if (t0 > 0 || !XF) {
             const int total = batch * pieces;
             __syncthreads();  // the previous block's LDS reads are done
             if (tid < batch) xrow_of[tid] = gperm[c0 + t0 + tid] / xdiv;
@@ -286,14 +294,15 @@ static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const 
     constexpr int ROWS = kMoeGemmWaves / KS * 16;
     const int64_t tiles = (a.n + ROWS - 1) / ROWS;
     static_assert(kPairsPerBlock == 16, "moe_gemm_x_lds assumes blocks of 16 pairs");
+    const dim3 grid((unsigned)tiles, (unsigned)a.experts);
     if (FMT == kNVFP4 && a.k % 32 != 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), dim3((unsigned)tiles, (unsigned)a.experts),
-                           dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale,
-                           goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
+        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), grid, dim3(kMoeGemmWaves * 64),
+                           (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff, gperm, a.x,
+                           a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
     else
-        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, false>), dim3((unsigned)tiles, (unsigned)a.experts),
-                           dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale,
-                           goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
+        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, false>), grid, dim3(kMoeGemmWaves * 64),
+                           (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff, gperm, a.x,
+                           a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
 // Register blocks per lane (MB) and k split (KS): the smallest capacity
