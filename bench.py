@@ -277,7 +277,9 @@ def main():
     # ---------------- MoE expert-indexed GEMV ----------------
     if "moe" in parts:
         moe = {}
-        nsets = 32
+        # 128 id sets on 128 bank copies: even the smallest launch (down, one token: 8 experts, 6.7 MB)
+        # gives a replay of 860 MB of distinct expert bytes, over three times the 256 MB MALL
+        nsets = 128
         for which in ("gate_up", "down"):
             case = synth.moe_layer(which, 1, seed=0)
             c0, s0 = u8(case["codes"]), u8(case["scales"])
