@@ -71,6 +71,7 @@ def _load():
         lib.orc_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, D, D, D, P, P, P]
         lib.orc_quantize.argtypes = [I, P, ctypes.c_float, I64, I64, P, P]
         lib.orc_requant_fp8.argtypes = [P, P, I64, I64, I64, I64, P, P]
+        lib.orc_split_e4m3.argtypes = [P, I64, I64, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -232,6 +233,21 @@ def requant_fp8(codes_in, tile_scales, n, k, bn=128, bk=128):
     scales = np.zeros((n, k // 32), dtype=np.uint8)
     _load().orc_requant_fp8(_ptr(codes_in), _ptr(tile_scales), n, k, bn, bk, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def split_e4m3(x, rows, k):
+    """Two-term E4M3 split of bf16 bits x [rows][k] (uint16), per 32-element block:
+    v = 2^e1 q1 + 2^e2 q2 + (remainder) with non-saturating scales (oracle.c).  Returns
+    (q1, q2 uint8 [rows][k] E4M3 codes, e1, e2 uint8 [rows][k/32] E8M0 bytes)."""
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    x = _c(x, np.uint16)
+    q1 = np.zeros((rows, k), dtype=np.uint8)
+    q2 = np.zeros((rows, k), dtype=np.uint8)
+    e1 = np.zeros((rows, k // 32), dtype=np.uint8)
+    e2 = np.zeros((rows, k // 32), dtype=np.uint8)
+    _load().orc_split_e4m3(_ptr(x), rows, k, _ptr(q1), _ptr(q2), _ptr(e1), _ptr(e2))
+    return q1, q2, e1, e2
 
 
 def within_tolerance(y_gpu, y_ref, abs_ref, rel=1e-5, atol=1e-6):

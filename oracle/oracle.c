@@ -552,3 +552,68 @@ void orc_requant_fp8(const uint8_t *codes_in, const float *tile_scales, int64_t 
         }
     }
 }
+
+/* ---- two-term E4M3 split of bf16 activations --------------------------------
+ *
+ * The "Plans ahead" section of the "MLxcel 0.8 release" post says CDNA 3/4
+ * parts have FP8/FP4 matrix hardware that wants its own kernel path.  gfx950's
+ * block-scaled matrix instruction takes both operands as FP8/FP6/FP4 codes
+ * with one E8M0 scale per 32 elements of k; the pages define no activation
+ * format for it.  Reading taken: each 32-element block of a bf16 activation
+ * row is written as a sum of two scaled E4M3 terms, which keeps the product
+ * the GEMM definition gives (the acceptance bound is met; see the split study
+ * in the tests):
+ *
+ *   e_t = the smallest integer e with amax_t <= 448 * 2^e, clamped to
+ *         [-127, 127] (amax_t = 0 takes -127); s_t = 2^e_t
+ *   amax_1 = max |v|;             q1 = q(v / s1)     (E4M3 rounding of the
+ *   r = v - s1 * q1 (exact);      amax_2 = max |r|;  q2 = q(r / s2)
+ *                                 quantizer above; |v / s_t| <= 448, so it never saturates)
+ *
+ * Codes carry the sign of v (term 1, so -0 gives 0x80) and of r (term 2, a zero
+ * residual is +0).  Outputs: q1, q2 uint8 [rows][k]; e1 + 127, e2 + 127 uint8
+ * [rows][k / 32].  k a multiple of 32; inputs finite. */
+static int orc_split_exponent(double amax)
+{
+    if (amax == 0.0) return -127;
+    int e;
+    (void)frexp(amax, &e);
+    e -= 9; /* floor(log2 amax) - 8: amax < 2^(e + 9) = 512 * 2^e */
+    while (amax > 448.0 * ldexp(1.0, e)) ++e;
+    while (e > -127 && amax <= 448.0 * ldexp(1.0, e - 1)) --e;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+void orc_split_e4m3(const uint16_t *x, int64_t rows, int64_t k, uint8_t *q1, uint8_t *q2, uint8_t *e1, uint8_t *e2)
+{
+    const int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t o = r * k + b * 32;
+            double v[32], res[32], amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                v[j] = orc_bf16(x[o + j]);
+                if (fabs(v[j]) > amax) amax = fabs(v[j]);
+            }
+            const int ea = orc_split_exponent(amax);
+            double amax2 = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                const double m = orc_quant_mag(fabs(v[j]) / ldexp(1.0, ea), 3, -6, 448.0);
+                const unsigned neg = (x[o + j] >> 15) & 1u;
+                q1[o + j] = (uint8_t)(orc_e4m3_code(m) | (neg << 7));
+                res[j] = v[j] - (neg ? -m : m) * ldexp(1.0, ea);
+                if (fabs(res[j]) > amax2) amax2 = fabs(res[j]);
+            }
+            const int eb = orc_split_exponent(amax2);
+            for (int j = 0; j < 32; ++j) {
+                const double m = orc_quant_mag(fabs(res[j]) / ldexp(1.0, eb), 3, -6, 448.0);
+                q2[o + j] = (uint8_t)(orc_e4m3_code(m) | ((res[j] < 0.0 ? 1u : 0u) << 7));
+            }
+            e1[r * nb + b] = (uint8_t)(ea + 127);
+            e2[r * nb + b] = (uint8_t)(eb + 127);
+        }
+    }
+}

@@ -728,6 +728,86 @@ def check_requant_roundtrip(seed=29):
     assert (sc == want).all()
 
 
+# ---- two-term E4M3 split of bf16 activations ------------------------------------------
+
+def _e4m3_book():
+    """Positive finite E4M3 codes 0x00 .. 0x7E and their values (decoded by the pinned oracle.e4m3)."""
+    codes = np.arange(0x7F)
+    return codes, np.array([oracle.e4m3(int(c)) for c in codes])
+
+
+def _split_bruteforce(v):
+    """Brute-force split of fp64 blocks v [nblocks][32]: each scale exponent found by searching
+    e = -127 .. 127 for the smallest with amax <= 448 * 2^e, each code by searching the E4M3
+    codebook for the nearest value (ties: the even code).  Returns (q1, q2, e1, e2) like
+    oracle.split_e4m3 (codes with sign bits, E8M0 bytes)."""
+    book_c, book_v = _e4m3_book()
+    es = np.arange(-127, 128)
+
+    def exponent(amax):
+        ok = amax[:, None] <= 448.0 * np.exp2(es)[None, :]
+        return np.where(ok.any(axis=1), es[np.argmax(ok, axis=1)], 127)
+
+    def nearest(t):  # t >= 0, fp64 -> index into the codebook (searched once per distinct value)
+        u, inv = np.unique(t, return_inverse=True)
+        d = np.abs(book_v[None, :] - u[:, None])
+        cand = d == d.min(axis=1, keepdims=True)
+        even = cand & (book_c[None, :] % 2 == 0)
+        pick = np.where(even.any(axis=1), np.argmax(even, axis=1), np.argmax(cand, axis=1))
+        return pick[inv.reshape(-1)].reshape(t.shape)
+
+    neg1 = np.signbit(v)
+    e1 = exponent(np.abs(v).max(axis=1))
+    i1 = nearest(np.abs(v) / np.exp2(e1)[:, None])
+    m1 = book_v[i1]
+    r = v - np.where(neg1, -m1, m1) * np.exp2(e1)[:, None]
+    e2 = exponent(np.abs(r).max(axis=1))
+    i2 = nearest(np.abs(r) / np.exp2(e2)[:, None])
+    q1 = (book_c[i1] | (neg1.astype(np.int64) << 7)).astype(np.uint8)
+    q2 = (book_c[i2] | ((r < 0).astype(np.int64) << 7)).astype(np.uint8)
+    return q1, q2, (e1 + 127).astype(np.uint8), (e2 + 127).astype(np.uint8)
+
+
+def _split_check(xbits):
+    rows, k = xbits.shape
+    got = oracle.split_e4m3(xbits, rows, k)
+    v = (xbits.astype(np.uint32) << 16).view(np.float32).astype(np.float64).reshape(-1, 32)
+    want = _split_bruteforce(v)
+    for name, g, w in zip(("q1", "q2", "e1", "e2"), got, want):
+        g = g.reshape(w.shape)
+        assert (g == w).all(), (name, np.argwhere(g != w)[:3], g[g != w][:3], w[g != w][:3])
+
+
+def check_split_every_bf16():
+    """Every finite bf16 value alone in a block (the other 31 elements zero, both signs of zero)."""
+    h = np.arange(65536, dtype=np.uint32)
+    finite = ((h >> 7) & 0xFF) != 0xFF
+    vals = h[finite].astype(np.uint16)
+    x = np.zeros((vals.size, 32), dtype=np.uint16)
+    x[:, 0] = vals
+    x[:, 17] = 0x8000  # -0 keeps its sign in term 1
+    _split_check(x)
+
+
+def check_split_mixed_blocks(seed=47):
+    """Blocks mixing magnitudes over many binades, subnormals, zeros and values near the bf16 top;
+    and the exactness the design relies on: N(0,1) activations are reproduced exactly by the two
+    terms for all but a small fraction of elements."""
+    rng = np.random.default_rng(seed)
+    rows = [(rng.standard_normal(64) * np.exp2(rng.integers(-30, 30, size=64))).tolist() for _ in range(8)]
+    rows.append([1e-39, -2e-40] + [0.0] * 62)
+    rows.append([3.0e38, -1.0] + [7.0] * 62)
+    rows.append([448.0, 449.0, 447.0, -0.0] * 16)
+    _split_check(_bits(rows))
+    x = _bits(rng.standard_normal((64, 256)).tolist())
+    q1, q2, e1, e2 = oracle.split_e4m3(x, 64, 256)
+    dec = np.vectorize(oracle.e4m3)
+    s1 = np.repeat(np.exp2(e1.astype(np.float64) - 127), 32, axis=1)
+    s2 = np.repeat(np.exp2(e2.astype(np.float64) - 127), 32, axis=1)
+    v = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert (dec(q1) * s1 + dec(q2) * s2 == v).mean() > 0.999
+
+
 def all_checks():
     """(name, callable) for every pin, used by the mutation test."""
     out = [("e2m1_table", check_e2m1_table), ("e8m0", check_e8m0), ("e4m3", check_e4m3),
@@ -749,4 +829,5 @@ def all_checks():
             ("quantize_roundtrip_mxfp4", lambda: check_quantize_roundtrip(MXFP4)),
             ("quantize_roundtrip_mxfp8", lambda: check_quantize_roundtrip(MXFP8)),
             ("requant_nearest", check_requant_nearest), ("requant_roundtrip", check_requant_roundtrip)]
+    out += [("split_every_bf16", check_split_every_bf16), ("split_mixed_blocks", check_split_mixed_blocks)]
     return out

@@ -67,6 +67,11 @@ MUTANTS = {
                            "                v[j] = (orc_e4m3(codes_in[r * k + col]) * s);"),
     "requant_emax": ("se = (e - 1) - 8;\n                if (se < -127) se = -127;\n                if (se > 127) se = 127;\n            }\n            scales[r * nb + b]",
                      "se = (e - 1) - 7;\n                if (se < -127) se = -127;\n                if (se > 127) se = 127;\n            }\n            scales[r * nb + b]"),
+    "split_saturating_scale": ("while (amax > 448.0 * ldexp(1.0, e)) ++e;", "while (0) ++e;"),
+    "split_no_second_term": ("const double m = orc_quant_mag(fabs(res[j]) / ldexp(1.0, eb), 3, -6, 448.0);",
+                             "const double m = 0.0;"),
+    "split_residual_sign": ("res[j] = v[j] - (neg ? -m : m) * ldexp(1.0, ea);", "res[j] = v[j] - m * ldexp(1.0, ea);"),
+    "split_term2_scale": ("const int eb = orc_split_exponent(amax2);", "const int eb = orc_split_exponent(amax);"),
     "requant_sign": ("(uint8_t)(orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)) | (neg << 7));",
                      "(uint8_t)(orc_e4m3_code(orc_quant_mag(fabs(p), 3, -6, 448.0)));"),
 }
@@ -91,7 +96,7 @@ def test_pins_reject_mutant(tmp_path, monkeypatch, name):
     mutant = ctypes.CDLL(path)
     for attr in ("orc_e2m1", "orc_e8m0", "orc_e4m3", "orc_bf16", "orc_num_threads", "orc_set_num_threads",
                  "orc_dequant", "orc_gemv", "orc_moe_gemv", "orc_gemm_rows", "orc_moe_route", "orc_silu",
-                 "orc_round_bf16", "orc_moe_block", "orc_quantize", "orc_requant_fp8"):
+                 "orc_round_bf16", "orc_moe_block", "orc_quantize", "orc_requant_fp8", "orc_split_e4m3"):
         fr, fm = getattr(real, attr), getattr(mutant, attr)
         fm.argtypes, fm.restype = fr.argtypes, fr.restype
     monkeypatch.setattr(oracle, "_lib", mutant)
