@@ -56,7 +56,6 @@ def lib() -> ctypes.CDLL:
         L.mxq_gemv_config.argtypes = [I, P, P, P, P, P, I64, I64, I64, ctypes.POINTER(GemvConfig), P]
         L.mxq_moe_gemv.argtypes = [I, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P]
         L.mxq_gemm.argtypes = [I, P, P, P, P, P, I, I64, I64, I64, P]
-        L.mxq_gemm_split.argtypes = [I, P, P, P, P, I, P, I64, I64, I64, P]
         L.mxq_dequant.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_moe_route.argtypes = [P, P, P, I64, I64, I64, I, P]
         L.mxq_moe_block.argtypes = [I, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
@@ -66,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.mxq_quantize.argtypes = [I, P, P, P, P, I64, I64, P]
         L.mxq_requant_fp8.argtypes = [P, P, P, P, I64, I64, I64, I64, P]
         L.mxq_stream_read.argtypes = [P, I64, I, P, I64, P]
-        for f in (L.mxq_gemv, L.mxq_gemv_config, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_gemm_split, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
+        for f in (L.mxq_gemv, L.mxq_gemv_config, L.mxq_moe_gemv, L.mxq_gemm, L.mxq_dequant, L.mxq_moe_route, L.mxq_moe_block,
                   L.mxq_moe_block_noalloc, L.mxq_moe_block_routed, L.mxq_moe_gemm, L.mxq_quantize, L.mxq_requant_fp8, L.mxq_stream_read):
             f.restype = I
         L.mxq_status_string.argtypes = [I]
@@ -343,49 +342,6 @@ def gemm(fmt, codes, scales, x, global_scale=None, out_dtype=torch.bfloat16, out
     ydt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     _check(lib().mxq_gemm(fmt, _ptr(codes), _ptr(scales), _ptr(global_scale), _ptr(x), _ptr(out), ydt, m, n, k,
                           _stream(stream)), "mxq_gemm")
-    return out
-
-
-def gemm_split_workspace_bytes(m, k):
-    """Bytes of mxq_gemm_split's workspace: 2 m k + 2 m k / 32."""
-    return 2 * m * k + 2 * m * (k // 32)
-
-
-def gemm_split_workspace_views(ws, m, k):
-    """(q1 [m, k], q2 [m, k], e1 [m, k/32], e2 [m, k/32]) uint8 views of a split-GEMM workspace."""
-    flat = ws.reshape(-1)
-    q1 = flat[:m * k].view(m, k)
-    q2 = flat[m * k:2 * m * k].view(m, k)
-    e1 = flat[2 * m * k:2 * m * k + m * (k // 32)].view(m, k // 32)
-    e2 = flat[2 * m * k + m * (k // 32):2 * m * k + 2 * m * (k // 32)].view(m, k // 32)
-    return q1, q2, e1, e2
-
-
-def gemm_split(codes, scales, x, out_dtype=torch.bfloat16, out=None, workspace=None, stream=None, fmt=MXFP4):
-    """Y[m][i] = sum_k X[m][k] * W[i][k] for MXFP4 W on the block-scaled matrix instruction: X split into two
-    scaled E4M3 terms per 32-element block (kept in `workspace`, uint8, gemm_split_workspace_bytes(m, k),
-    allocated when None), W's codes used as they are.  -> [m, n] in float32 or bfloat16 (RNE)."""
-    codes = _dev(codes, torch.uint8, "codes")
-    scales = _dev(scales, torch.uint8, "scales")
-    x = _dev(x, torch.bfloat16, "x")
-    k = _check_weight(fmt, codes, scales, None)
-    n = codes.shape[0]
-    if x.dim() != 2 or x.shape[1] != k:
-        raise ValueError(f"x must be [m, {k}], got {tuple(x.shape)}")
-    m = x.shape[0]
-    if workspace is None:
-        workspace = torch.empty(gemm_split_workspace_bytes(m, k), dtype=torch.uint8, device=codes.device)
-    workspace = _dev(workspace, torch.uint8, "workspace")
-    if workspace.numel() < gemm_split_workspace_bytes(m, k):
-        raise ValueError(f"workspace must hold {gemm_split_workspace_bytes(m, k)} bytes")
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=codes.device)
-    out = _dev(out, out_dtype, "out")
-    if out.numel() != m * n:
-        raise ValueError("out must hold m * n elements")
-    ydt = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
-    _check(lib().mxq_gemm_split(fmt, _ptr(codes), _ptr(scales), _ptr(x), _ptr(out), ydt, _ptr(workspace), m, n, k,
-                                _stream(stream)), "mxq_gemm_split")
     return out
 
 

@@ -92,7 +92,7 @@ MXQ_API const char* mxq_status_string(int s) {
     return "unknown status";
 }
 
-MXQ_API int mxq_abi_version(void) { return 10; }
+MXQ_API int mxq_abi_version(void) { return 9; }
 
 MXQ_API mxq_status_t mxq_gemv(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,
                               const uint16_t* x, float* y, int64_t n, int64_t k, int64_t batch, void* stream) {
@@ -202,32 +202,6 @@ MXQ_API mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t* codes, const uint
     }
     const mxq::GemmArgs a{fmt, codes, scales, global_scale, x, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k};
     return launched(mxq::launch_gemm(a, as_stream(stream)));
-}
-
-MXQ_API mxq_status_t mxq_gemm_split(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
-                                    void* y, mxq_out_t y_dtype, uint8_t* workspace, int64_t m, int64_t n, int64_t k,
-                                    void* stream) {
-    if (fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_MXFP8 && fmt != MXQ_FMT_NVFP4) return MXQ_E_FORMAT;
-    if (y_dtype != MXQ_OUT_F32 && y_dtype != MXQ_OUT_BF16) return MXQ_E_FORMAT;
-    if (!codes || !scales || !x || !y || !workspace) return MXQ_E_NULLPTR;
-    if (m <= 0 || n <= 0 || k <= 0) return MXQ_E_SHAPE;
-    mxq_status_t st;
-    if ((st = check_k(MXQ_FMT_MXFP4, k)) != MXQ_OK) return st;
-    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 16)) return MXQ_E_ALIGN;
-    if (fmt != MXQ_FMT_MXFP4) return MXQ_E_UNSUPPORTED;  // the instruction takes E8M0 block scales of 32
-    // the kernel addresses one tile's rows with 32-bit offsets: 256 rows of k bytes
-    if (m > kMaxDim || n > kMaxDim || k > (int64_t(1) << 22)) return MXQ_E_UNSUPPORTED;
-    if (((m + 255) / 256) * ((n + 255) / 256) > kMaxDim) return MXQ_E_UNSUPPORTED;
-    int cus = 0;
-    if ((st = check_device(&cus)) != MXQ_OK) return st;
-    uint8_t* q1 = workspace;
-    uint8_t* q2 = q1 + m * k;
-    uint8_t* e1 = q2 + m * k;
-    uint8_t* e2 = e1 + m * (k / 32);
-    const mxq::SplitArgs sp{x, q1, q2, e1, e2, m, k};
-    if ((st = launched(mxq::launch_split_e4m3(sp, as_stream(stream)))) != MXQ_OK) return st;
-    const mxq::GemmSplitArgs a{codes, scales, q1, q2, e1, e2, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k};
-    return launched(mxq::launch_gemm_split(a, as_stream(stream)));
 }
 
 MXQ_API mxq_status_t mxq_dequant(mxq_format_t fmt, const uint8_t* codes, const uint8_t* scales, const float* global_scale,

@@ -293,213 +293,6 @@ static void launch_gemm_inst(const GemmArgs& a, hipStream_t st) {
                            a.scales, a.gscale, a.x, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
 }
 
-// ---- the block-scaled variant: split activations x MXFP4 weights --------------------
-//
-// gfx950's block-scaled matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4)
-// multiplies FP8/FP6/FP4 codes with one E8M0 scale per 32 k of each operand;
-// the "Plans ahead" section of the "MLxcel 0.8 release" post names such FP8/FP4
-// hardware as the next kernel path.  Here A is the activations' two-term E4M3
-// split (quantize.hip: x = 2^e1 q1 + 2^e2 q2 per 32-block) and B the MXFP4
-// weight codes with their own E8M0 bytes, so the weights are never decoded:
-// each k step of 64 is two instructions (one per term) into the same fp32
-// accumulators.  The instruction runs FP8 x FP4 at twice the bf16 rate, so
-// the two terms take the bf16 path's matrix time; what goes is the decode.
-//
-// Tiles, waves, tile order and pipelining are those of gemm_kernel above (256
-// x 256 per workgroup, 8 waves of 128 x 64, one 64-wide k slice per stage).
-// Operand layouts of the instruction (measured on MI355X with known inputs):
-//  * B (32 columns x 64 k, FP4): lane (l32, h = lane / 32) holds column l32,
-//    k = 32 h + j in nibble j (low nibble first) -- one 16-byte MXFP4 block of
-//    the weight row -- and the scale operand of lane (l32, h) is that block's
-//    E8M0 byte.
-//  * A (32 rows x 64 k, FP8): lane (l32, h) holds row l32, bytes 0..15 at
-//    k = 16 h + j and bytes 16..31 at k = 32 + 16 h + (j - 16); the scale
-//    operand of lane (l32, h) is the E8M0 byte of row l32's block h (k = 32 h
-//    .. 32 h + 31), the byte selected by the instruction's operand select.
-//  * D: as the bf16 32x32 instruction (rows 8 r + 4 h + q in element 4 r + q).
-// The X slices sit in LDS as [term][256 rows][64 + 16 bytes] (the 16-byte pad
-// spreads 16 rows' reads over distinct banks) plus [256 rows][4] scale bytes
-// (e1 of the slice's blocks 0 and 1, then e2's).
-constexpr int kSplitBK = 64;
-constexpr int kSplitStride = kSplitBK + 16;                 // bytes per LDS row of a term
-constexpr int kSplitTerm = kBM * kSplitStride;              // bytes per term tile
-constexpr int kSplitBuf = 2 * kSplitTerm + kBM * 4;         // both terms and the scales
-constexpr int kSplitPieces = 2 * kBM * kSplitBK / 16 / kGemmThreads;  // 16-byte pieces per thread
-
-__global__ __launch_bounds__(kGemmThreads) void gemm_split_kernel(const uint8_t* __restrict__ codes,
-                                                                  const uint8_t* __restrict__ scales,
-                                                                  const uint8_t* __restrict__ q1,
-                                                                  const uint8_t* __restrict__ q2,
-                                                                  const uint8_t* __restrict__ e1,
-                                                                  const uint8_t* __restrict__ e2,
-                                                                  void* __restrict__ yv, int y_bf16, int64_t m,
-                                                                  int64_t n, int64_t k, int xcd_order) {
-    typedef int v8i_t __attribute__((ext_vector_type(8)));
-    extern __shared__ __attribute__((aligned(16))) uint8_t sl[];  // [2][kSplitBuf]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int64_t mt = (m + kBM - 1) / kBM, nt = (n + kBN - 1) / kBN;
-    int64_t tm, tn;
-    if (xcd_order) tile_of(blockIdx.x, mt, nt, tm, tn);
-    else { tm = blockIdx.x / nt; tn = blockIdx.x % nt; }
-    const int64_t m0 = tm * kBM, n0 = tn * kBN;
-    const int64_t rowbytes = k / 2, sbytes = k / 32, nblk = k / 32;
-
-    // X loader: piece p = tid + kGemmThreads * u is term p / 1024, row (p / 4) % 256,
-    // 16-byte column p % 4 of the slice; thread t < 256 also copies row t's four scale bytes.
-    // piece u of this thread: term u / 2, row (tid / 4 + 128 u) % 256 of the tile, column tid % 4;
-    // offsets from the tile's first row (the rows of the tile span less than 2^32 bytes)
-    const uint8_t* xb1 = q1 + m0 * k;
-    const uint8_t* xb2 = q2 + m0 * k;
-    uint32_t xoff[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        int64_t r = m0 + (tid >> 2) + 128 * u;
-        r = r < m ? r : m - 1;  // rows past m read row m-1; their outputs are not written
-        xoff[u] = (uint32_t)((r - m0) * k + (tid & 3) * 16);
-    }
-    int64_t srow_x = m0 + (tid & (kBM - 1));
-    srow_x = srow_x < m ? srow_x : m - 1;
-    const uint8_t* esrc = (tid < kBM ? e1 : e2) + srow_x * nblk;
-    u32x4g_t xr[kSplitPieces];
-    uint32_t er;  // two scale bytes of this thread's row and term
-    auto load_x = [&](int64_t k0) {
-#pragma unroll
-        for (int u = 0; u < kSplitPieces; ++u) {
-            const int p = tid + kGemmThreads * u;
-            if (k0 + (p & 3) * 16 < k)
-                xr[u] = *reinterpret_cast<const u32x4g_t*>(((u >> 1) ? xb2 : xb1) + xoff[u & 1] + k0);
-            else xr[u] = u32x4g_t{0u, 0u, 0u, 0u};
-        }
-        const int64_t b0 = k0 / 32;
-        er = (uint32_t)esrc[b0] | ((b0 + 1 < nblk ? (uint32_t)esrc[b0 + 1] : 127u) << 8);
-    };
-    auto store_x = [&](int buf) {
-        uint8_t* base = sl + buf * kSplitBuf;
-#pragma unroll
-        for (int u = 0; u < kSplitPieces; ++u) {
-            const int p = tid + kGemmThreads * u;
-            *reinterpret_cast<u32x4g_t*>(base + (p >> 10) * kSplitTerm + ((p >> 2) % kBM) * kSplitStride +
-                                         (p & 3) * 16) = xr[u];
-        }
-        *reinterpret_cast<uint16_t*>(base + 2 * kSplitTerm + (tid & (kBM - 1)) * 4 + (tid >= kBM ? 2 : 0)) =
-            (uint16_t)er;
-    };
-    // W: this lane's block (column n0 + wn*64 + j*32 + l32, k block k0/32 + half), as gemm_kernel
-    const uint8_t* cb = codes + n0 * rowbytes;
-    const uint8_t* sb = scales + n0 * sbytes;
-    uint32_t coff[2], soff[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        int64_t r = n0 + wn * 64 + j * 32 + l32;
-        r = r < n ? r : n - 1;
-        coff[j] = (uint32_t)((r - n0) * rowbytes);
-        soff[j] = (uint32_t)((r - n0) * sbytes);
-    }
-    using Frag = WFrag<kMXFP4, 32>;
-    auto load_w = [&](int64_t k0, Frag (&wf)[2]) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) load_wfrag<kMXFP4, 32, false>(cb + coff[j], sb + soff[j], k0 + half * 32, k, wf[j]);
-    };
-
-    f32x16_t acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    auto mfma_slice = [&](int buf, const Frag (&wf)[2]) {
-        const uint8_t* base = sl + buf * kSplitBuf;
-        v8i_t bo[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bo[j] = v8i_t{(int)wf[j].w[0], (int)wf[j].w[1], (int)wf[j].w[2], (int)wf[j].w[3], 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + i * 32 + l32;
-            // this lane's block-h scales: e1 in byte 0, e2 in byte 2
-            const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + 2 * kSplitTerm + row * 4) >> (8 * half);
-            const uint8_t* ar = base + row * kSplitStride + half * 16;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x4g_t lo = *reinterpret_cast<const u32x4g_t*>(ar + t * kSplitTerm);
-                const u32x4g_t hi = *reinterpret_cast<const u32x4g_t*>(ar + t * kSplitTerm + 32);
-                const v8i_t a = v8i_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (t == 0)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bo[j], acc[i][j], 0, 4, 0,
-                                                                                     (int)sa, 0, (int)wf[j].s);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bo[j], acc[i][j], 0, 4, 2,
-                                                                                     (int)sa, 0, (int)wf[j].s);
-                }
-            }
-
-        }
-        // the products are pinned before what follows (the next slice's stores,
-        // loads and barrier): otherwise the compiler may sink them past it and
-        // keep every operand of the slice live at once
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
-    };
-
-    const int64_t nk = (k + kSplitBK - 1) / kSplitBK;
-    const int64_t klast = (nk - 1) * kSplitBK;
-    auto kof = [&](int64_t s) { return s < nk ? s * kSplitBK : klast; };
-    Frag wa[2], wb[2];
-    load_x(0);
-    load_w(0, wa);
-    store_x(0);
-    load_x(kof(1));
-    load_w(kof(1), wb);
-    lds_barrier();
-    for (int64_t s = 0; s < nk; ++s) {
-        const int buf = (int)(s & 1);
-        mfma_slice(buf, wa);
-        store_x(buf ^ 1);  // slice s+1
-        load_x(kof(s + 2));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) wa[j] = wb[j];
-        load_w(kof(s + 2), wb);
-        lds_barrier();
-    }
-
-    const int64_t rbase = m0 + wm * 128 + half * 4, cbase = n0 + wn * 64 + l32;
-    const bool full = (m0 + kBM <= m) && (n0 + kBN <= n);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t col = cbase + j * 32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = rbase + i * 32 + (e >> 2) * 8 + (e & 3);
-                if (!full && (row >= m || col >= n)) continue;
-                const float v = acc[i][j][e];
-                if (y_bf16) reinterpret_cast<uint16_t*>(yv)[row * n + col] = f32_to_bf16_rne(v);
-                else reinterpret_cast<float*>(yv)[row * n + col] = v;
-            }
-        }
-}
-
-bool launch_gemm_split(const GemmSplitArgs& a, hipStream_t st) {
-    const int64_t mt = (a.m + kBM - 1) / kBM, nt = (a.n + kBN - 1) / kBN;
-    const int64_t tiles = mt * nt;
-    const int xcd_order = (tiles % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(gemm_split_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), (size_t)(2 * kSplitBuf), st,
-                       a.codes, a.scales, a.q1, a.q2, a.e1, a.e2, a.y, a.y_bf16, a.m, a.n, a.k, xcd_order);
-    return true;
-}
-
 bool launch_gemm(const GemmArgs& a, hipStream_t st) {
     switch (a.fmt) {
         case kMXFP4: launch_gemm_inst<kMXFP4>(a, st); return true;

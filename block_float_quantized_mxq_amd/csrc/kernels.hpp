@@ -176,35 +176,6 @@ struct RequantArgs {
 };
 bool launch_requant_fp8(const RequantArgs& a, hipStream_t st);
 
-// Two-term E4M3 split of bf16 activations x[rows][k] (k a multiple of 32):
-// codes q1, q2 [rows][k] and E8M0 bytes e1, e2 [rows][k/32].
-struct SplitArgs {
-    const uint16_t* x;
-    uint8_t* q1;
-    uint8_t* q2;
-    uint8_t* e1;
-    uint8_t* e2;
-    int64_t rows, k;
-};
-bool launch_split_e4m3(const SplitArgs& a, hipStream_t st);
-
-// Prefill GEMM on the block-scaled matrix instruction: MXFP4 weights against
-// the split activations (two FP8 x FP4 products per k step).
-struct GemmSplitArgs {
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const uint8_t* q1;
-    const uint8_t* q2;
-    const uint8_t* e1;
-    const uint8_t* e2;
-    void* y;
-    int y_bf16;
-    int64_t m, n, k;
-};
-bool launch_gemm_split(const GemmSplitArgs& a, hipStream_t st);
-// Its workspace: q1, q2 (m k bytes each), then e1, e2 (m k / 32 bytes each).
-constexpr int64_t gemm_split_workspace_bytes(int64_t m, int64_t k) { return 2 * m * k + 2 * m * (k / 32); }
-
 // Streaming read of `bytes` (a multiple of 16) on `workgroups` workgroups,
 // lanes interleaved over the range or one contiguous range per workgroup;
 // sink[w] receives workgroup w's fold of the words it read.

@@ -197,84 +197,6 @@ bool launch_quantize(const QuantizeArgs& a, hipStream_t st) {
     return false;
 }
 
-// ---- two-term E4M3 split of bf16 activations -----------------------------------------
-//
-// The A operand of the block-scaled GEMM (gemm.hip): each block of 32 bf16
-// values v is written as 2^e1 q1 + 2^e2 q2 with E4M3 codes.  e1 is the
-// smallest exponent with amax <= 448 * 2^e1 (clamped to [-127, 127]; zero and
-// subnormal maxima take -127, which already covers them), so v * 2^-e1 never
-// exceeds 448 and its rounding never saturates; q1 = E4M3(v * 2^-e1).  The
-// residual r = v - q1 2^e1 is exact in fp32 (both are multiples of the
-// finer of the two grids and |r| is below the coarser grid's spacing), and is
-// split the same way into e2, q2.  One lane per block, like the quantizer.
-
-// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127] (amax >= 0, a
-// bf16 value or an exact residual): amax = (1 + f) 2^E needs e = E - 8, or
-// E - 7 when 1 + f > 1.75.
-__device__ __forceinline__ int split_exponent(float amax) {
-    const uint32_t b = __builtin_bit_cast(uint32_t, amax);
-    const int ef = (int)(b >> 23);
-    if (ef == 0) return -127;  // zero or subnormal: below 448 * 2^-127
-    const int e = ef - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    return e < -127 ? -127 : e;  // a finite amax gives e <= 120
-}
-
-__global__ __launch_bounds__(256) void split_e4m3_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q1,
-                                                         uint8_t* __restrict__ q2, uint8_t* __restrict__ e1,
-                                                         uint8_t* __restrict__ e2, int64_t rows, int64_t k) {
-    const int64_t nb = k / 32;
-    for (int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x; blk < rows * nb; blk += (int64_t)gridDim.x * 256) {
-        const int64_t r = blk / nb, b = blk % nb;
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + r * k + b * 32);
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4_t w = src[i];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                v[8 * i + 2 * d] = bf16_lo_to_f32(w[d]);
-                v[8 * i + 2 * d + 1] = bf16_hi_to_f32(w[d]);
-            }
-        }
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
-        const int ea = split_exponent(amax);
-        float p[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) p[j] = __builtin_amdgcn_ldexpf(v[j], -ea);
-        uint32_t c1[8] = {};
-        e4m3_block_codes(p, c1);
-        // the residual: v minus the rounded term (the rounding the codes carry)
-        float amax2 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const float q = __builtin_copysignf(quant_mag(__builtin_fabsf(p[j]), 3, -6, 448.0f), v[j]);
-            v[j] = v[j] - __builtin_amdgcn_ldexpf(q, ea);
-            amax2 = __builtin_fmaxf(amax2, __builtin_fabsf(v[j]));
-        }
-        const int eb = split_exponent(amax2);
-#pragma unroll
-        for (int j = 0; j < 32; ++j) p[j] = __builtin_amdgcn_ldexpf(v[j], -eb);
-        uint32_t c2[8] = {};
-        e4m3_block_codes(p, c2);
-        u32x4_t* d1 = reinterpret_cast<u32x4_t*>(q1 + r * k + b * 32);
-        u32x4_t* d2 = reinterpret_cast<u32x4_t*>(q2 + r * k + b * 32);
-        d1[0] = u32x4_t{c1[0], c1[1], c1[2], c1[3]};
-        d1[1] = u32x4_t{c1[4], c1[5], c1[6], c1[7]};
-        d2[0] = u32x4_t{c2[0], c2[1], c2[2], c2[3]};
-        d2[1] = u32x4_t{c2[4], c2[5], c2[6], c2[7]};
-        e1[blk] = (uint8_t)(ea + 127);
-        e2[blk] = (uint8_t)(eb + 127);
-    }
-}
-
-bool launch_split_e4m3(const SplitArgs& a, hipStream_t st) {
-    const int64_t nb = a.rows * (a.k / 32);
-    hipLaunchKernelGGL(split_e4m3_kernel, block_grid(nb), dim3(256), 0, st, a.x, a.q1, a.q2, a.e1, a.e2, a.rows, a.k);
-    return true;
-}
-
 // ---- FP8 block checkpoint -> MXFP8 ------------------------------------------------
 //
 // The ROCm status table of the "Build from source" manual (section "Current

@@ -189,29 +189,6 @@ mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t *codes, const uint8_t *sca
                       const uint16_t *x, void *y, mxq_out_t y_dtype, int64_t m, int64_t n, int64_t k, void *stream);
 
 /*
- * The prefill GEMM on gfx950's block-scaled matrix instruction (the FP8/FP4
- * hardware that the "Plans ahead" section of the "MLxcel 0.8 release" post
- * names as the next kernel path): the same Y as mxq_gemm, without decoding W.
- * Each 32-element block of a row of X is first split into two scaled E4M3
- * terms, x = 2^e1 q1 + 2^e2 q2, e_t the smallest exponent that keeps the block
- * (then its residual) under 448, so no code saturates; the instruction then
- * multiplies q1 and q2 with the E2M1 codes of W, each operand with its E8M0
- * block scales, into fp32 accumulators.  The split reproduces N(0,1) bf16
- * activations exactly for all but a few elements, and Y stays within the
- * acceptance bound 1e-5 * sum|w x| + 1e-6 of the exact product; it is not
- * bit-identical to mxq_gemm's.
- *   fmt        MXQ_FMT_MXFP4 (the other formats: MXQ_E_UNSUPPORTED)
- *   codes/scales, x, y, y_dtype as mxq_gemm (no per-tensor scale)
- *   workspace  caller-owned, 16-byte aligned, 2 m k + 2 m k / 32 bytes: the
- *              split, left holding q1 [m][k], q2 [m][k] (E4M3 codes), then the
- *              E8M0 bytes e1 + 127 [m][k/32] and e2 + 127 [m][k/32]
- *   m, n >= 1, < 2^31; k a multiple of 32, at most 2^22
- */
-mxq_status_t mxq_gemm_split(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const uint16_t *x,
-                            void *y, mxq_out_t y_dtype, uint8_t *workspace, int64_t m, int64_t n, int64_t k,
-                            void *stream);
-
-/*
  * Decoded weights, for checking the in-kernel decode bit for bit:
  *   w[r][j] = fl32(q * 2^(u-127))        MX formats
  *   w[r][j] = fl32((q * s) * g)          NVFP4 (q*s is exact; one rounding)
@@ -410,7 +387,7 @@ mxq_status_t mxq_stream_read(const void *data, int64_t bytes, int layout, uint32
 /* Static description of a status code (never NULL). */
 const char *mxq_status_string(int status);
 
-/* ABI version of this header: 10 (mxq_moe_block_routed, then mxq_gemm_split, added to 8). */
+/* ABI version of this header: 9 (mxq_moe_block_routed added to 8). */
 int mxq_abi_version(void);
 
 #ifdef __cplusplus

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["mxq_gemv", "mxq_gemv_config", "mxq_moe_gemv", "mxq_gemm", "mxq_gemm_split", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
+        ["mxq_gemv", "mxq_gemv_config", "mxq_moe_gemv", "mxq_gemm", "mxq_dequant", "mxq_moe_route", "mxq_moe_block",
          "mxq_moe_block_noalloc", "mxq_moe_block_routed", "mxq_moe_gemm", "mxq_quantize", "mxq_requant_fp8", "mxq_stream_read",
          "mxq_status_string",
          "mxq_abi_version"])
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert lib.mxq_abi_version() == 10
+    assert lib.mxq_abi_version() == 9
 
 
 def test_status_strings():
@@ -76,25 +76,6 @@ def block_na(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=Non
              E=4, hidden=64, dff=64, T=1, topk=2):
     return mxq.lib().mxq_moe_block_noalloc(fmt, codes, scales, g, dn_codes, dn_scales, dn_g, ids, w, x, y,
                                            E, hidden, dff, T, topk, None)
-
-
-def gsplit(fmt=1, codes=A, scales=A, x=A, y=A, ydt=0, ws=A, m=4, n=8, k=64):
-    return mxq.lib().mxq_gemm_split(fmt, codes, scales, x, y, ydt, ws, m, n, k, None)
-
-
-def test_gemm_split_argument_errors():
-    assert gsplit(fmt=0) == FORMAT and gsplit(ydt=2) == FORMAT
-    for arg in ("codes", "scales", "x", "y", "ws"):
-        assert gsplit(**{arg: None}) == NULLPTR, arg
-    for arg in ("m", "n", "k"):
-        assert gsplit(**{arg: 0}) == SHAPE and gsplit(**{arg: -1}) == SHAPE, arg
-    assert gsplit(k=48) == SHAPE                                            # whole 32-element blocks
-    for arg, off in (("codes", 8), ("x", 8), ("y", 2), ("ws", 8)):
-        assert gsplit(**{arg: A + off}) == ALIGN, arg
-    assert gsplit(fmt=2) == UNSUPPORTED and gsplit(fmt=3) == UNSUPPORTED     # E8M0 blocks of 32 only
-    assert gsplit(k=(1 << 22) + 32) == UNSUPPORTED and gsplit(m=1 << 31) == UNSUPPORTED
-    if _no_gpu():
-        assert gsplit() == DEVICE and gsplit(k=1 << 22) == DEVICE
 
 
 def block_rt(fmt=1, codes=A, scales=A, g=None, dn_codes=A, dn_scales=A, dn_g=None, logits=A, renorm=0, ids=A, w=A,

@@ -17,7 +17,10 @@ Findings (recorded in the design notes):
   * two terms with a scale that never saturates (ceil(log2(amax / 448))) meet it
     with a wide margin (the split is exact for all but a few elements);
   * the scaled instruction runs FP8 x FP4 at the FP8 rate, 2x the bf16 rate, so
-    two terms cost what the bf16 MFMAs cost: no faster by rate, hence not built.
+    two terms cost what the bf16 MFMAs cost.  A GEMM built on it (measured on
+    MI355X) was slower than the bf16 path, and the instruction's own
+    accumulation drops low-order bits when one instruction's products span the
+    full E4M3 range, so it is not part of the library.
 """
 import numpy as np
 import pytest
