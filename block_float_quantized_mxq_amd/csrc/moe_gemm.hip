@@ -3,12 +3,16 @@
 //
 // The "Decoding block-float formats in software" section of the "MLxcel 0.8
 // release" post credits its MXFP4 MoE prefill gain to kernels that work expert
-// by expert.  Two kernels:
+// by expert.  Kernels:
 //
 //  * moe_group_kernel groups the pairs by expert (counts, prefix sums, and a
 //    permutation of the pairs) in a caller workspace, on the GPU, so nothing
 //    waits for the host.
-//  * moe_gemm_kernel: grid (row tile, expert).  Each wave loads its 16 weight
+//  * moe_gemm_stream_kernel (E2M1 codes, rows of whole 32-element blocks):
+//    the expert's weight rows stream through registers slice by slice against
+//    its pairs' inputs gathered into LDS (below).
+//  * moe_gemm_kernel (E4M3 codes, and NVFP4 rows of an odd number of 16-element
+//    blocks): grid (row tile, expert).  Each wave loads its 16 weight
 //    rows (over its k range) into registers once; the workgroup then walks
 //    the expert's pairs in blocks of 16, gathers their input rows into LDS and
 //    runs 16 x 16 x 32 bf16 MFMAs with the 16 pairs as the B operand's columns
@@ -23,6 +27,7 @@
 #include "block_operand.hpp"
 #include "gemv_mfma.hpp"
 #include "kernels.hpp"
+#include "rows_core.hpp"
 
 namespace mxq {
 
@@ -289,59 +294,230 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
     }
 }
 
+// ---- streaming variant (E2M1 codes, whole 32-element blocks) -------------------------
+//
+// Grid (tile of 256 weight rows, expert).  Wave w owns weight rows tile*256 +
+// 32w .. +31, one 32-row block of 32x32x16 bf16 MFMAs (the B operand's
+// columns); the expert's pairs are taken 64 at a time, two 32-pair blocks as
+// the A operand's rows.  Per 64-wide k slice the workgroup gathers the 64
+// pairs' inputs into LDS (double buffered; one 16-byte piece per thread) and
+// every wave multiplies them with its rows' codes, decoded to bf16 in
+// registers; lane (l32, h) holds the 32-element block h of the slice of its
+// row l32 (the k order of gemm.hip).  Codes and gathered inputs stream through
+// rings of slices in registers, each slot refilled as soon as it is used, so
+// a wave keeps loads in flight from start to end, as the GEMV engine does; the register-resident kernel above instead
+// loads its whole tile first and then computes, and two such workgroups per
+// CU leave HBM idle while both compute.
+typedef float f32x16m_t __attribute__((ext_vector_type(16)));
+// Slices in flight: kMgDepthW of codes per lane, kMgDepthX of gathered inputs
+// per thread (kMgDepthW divides kMgDepthX, the loop's unroll).  MI355X,
+// 30B-A3B banks, 512 tokens x top-8, MXFP4 gate/up / down: 92 / 53 us with two
+// of each (NVFP4 110 / 59); inputs four ahead 92 / 53 (NVFP4 115 / 59); with
+// inputs one ahead, and before the loop's branches and full waits went, 129 / 55.
+constexpr int kMgRows = 256, kMgPairs = 64, kMgBK = 64, kMgDepthW = 2, kMgDepthX = 2;
+static_assert(kMgDepthX % kMgDepthW == 0, "the unrolled loop indexes both rings statically");
+constexpr int kMgXStride = kMgBK + 8;  // bf16 per LDS row (16-byte pad: 16 rows' reads hit distinct banks)
+
+template <int FMT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_stream_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
+    const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
+    int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
+    static_assert(FMT != kMXFP8, "E2M1 codes: one 16-byte block per lane and slice");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kMgPairs * kMgXStride];
+    __shared__ int64_t xrow[kMgPairs];  // input row of each pair of the pass, -1 past its end
+    __shared__ int64_t qid[kMgPairs];   // output row (pair index) of each pair of the pass
+
+    const int64_t e = blockIdx.y;
+    const int64_t c0 = goff[e];
+    const int64_t cnt = goff[e + 1] - c0;
+    if (cnt <= 0) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int64_t rowbytes = code_bytes_per_row(FMT, k);
+    const int64_t sbytes = k / block_elems(FMT);
+    const int64_t r0 = (int64_t)blockIdx.x * kMgRows + wave * 32;
+    const int64_t wrow = r0 + l32 < n ? r0 + l32 : n - 1;
+    const uint8_t* crow = codes + (e * n + wrow) * rowbytes;
+    const uint8_t* srow = scales + (e * n + wrow) * sbytes;
+    const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
+    const int64_t nk = (k + kMgBK - 1) / kMgBK;
+    const int gp = tid >> 3, gc = tid & 7;  // gather: pair gp, columns 8 gc .. 8 gc + 7 of the slice
+
+    using Frag = WFrag<FMT, 32>;
+    for (int64_t p0 = 0; p0 < cnt; p0 += kMgPairs) {
+        const int np = (int)(cnt - p0 < kMgPairs ? cnt - p0 : kMgPairs);
+        __syncthreads();  // the previous pass is done with xrow, qid and xs
+        if (tid < kMgPairs) {
+            const int64_t q = tid < np ? gperm[c0 + p0 + tid] : -1;
+            qid[tid] = q;
+            xrow[tid] = q >= 0 ? q / xdiv : -1;
+        }
+        __syncthreads();
+        const int64_t xr = xrow[gp];
+        // Loads without branches and without touching their results until needed (a
+        // branch around a load, or a select right after it, makes the compiler wait for
+        // every load in flight): addresses clamped into the tensors, the values
+        // selected away past k or past the pass's pairs only where they are used.
+        auto gather = [&](int64_t k0) {
+            const int64_t kk = k0 + 8 * gc;
+            const bool ok = xr >= 0 && kk < k;
+            return *reinterpret_cast<const u32x4g_t*>(x + (ok ? xr * k + kk : 0));
+        };
+        auto put = [&](int buf, int64_t k0, const u32x4g_t& v) {  // v = gather(k0)
+            const bool ok = xr >= 0 && k0 + 8 * gc < k;
+            *reinterpret_cast<u32x4g_t*>(&xs[buf][gp * kMgXStride + 8 * gc]) = ok ? v : u32x4g_t{0u, 0u, 0u, 0u};
+        };
+        // this lane's block of slice s (cached loads: the other blocks of each 128-byte
+        // line come with the next slices); past k, zero codes and a unit scale are
+        // selected when the block is decoded
+        auto load_w = [&](int64_t s, Frag& f) {
+            const int64_t kb = s * kMgBK + half * 32;
+            const int64_t kc = kb < k ? kb : 0;
+            const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kc / 2);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) f.w[d] = v[d];
+            if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
+            else f.s = srow[kc / 32];
+        };
+        auto live = [&](int64_t s, const Frag& f) {
+            const bool ok = s * kMgBK + half * 32 < k;
+            Frag g;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) g.w[d] = ok ? f.w[d] : 0u;
+            g.s = ok ? f.s : (FMT == kNVFP4 ? 0x3838u : 127u);
+            return g;
+        };
+        // the rings: slice j's codes in ring[j % kMgDepthW]; its gathered inputs in
+        // xq[j % kMgDepthX] until stored to LDS at the end of slice j - 1.  Slices are
+        // taken kMgDepthX at a time; those past the last one multiply zeros.
+        Frag ring[kMgDepthW];
+        static_for<0, kMgDepthW>([&](auto J) { load_w(J, ring[J]); });
+        u32x4g_t xq[kMgDepthX];
+        put(0, 0, gather(0));
+        static_for<1, kMgDepthX>([&](auto J) { xq[J] = gather((int64_t)J * kMgBK); });
+        // barriers wait for LDS traffic only (__syncthreads would also wait for every
+        // global load in flight, draining the rings at each slice)
+        lds_barrier();
+        f32x16m_t acc[2];
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[pb][i] = 0.0f;
+        const bool two = np > 32;  // wave uniform
+        for (int64_t s0 = 0; s0 < nk; s0 += kMgDepthX) {
+            static_for<0, kMgDepthX>([&](auto J) {
+                const int64_t s = s0 + J;
+                constexpr int JW = decltype(J)::value % kMgDepthW;
+                xq[J] = gather((s + kMgDepthX) * kMgBK);
+                const uint16_t* as = &xs[s & 1][l32 * kMgXStride + half * 32];
+                const Frag w = live(s, ring[JW]);
+                static_for<0, 4>([&](auto S) {
+                    const bf16x8_t b = decode_step<FMT, decltype(S)::value>(w);
+                    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(as + S * 8);
+                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+                    if (two) {
+                        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(as + 32 * kMgXStride + S * 8);
+                        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+                    }
+                });
+                load_w(s + kMgDepthW, ring[JW]);
+                put((int)((s + 1) & 1), (s + 1) * kMgBK, xq[(decltype(J)::value + 1) % kMgDepthX]);
+                lds_barrier();
+            });
+        }
+        // acc[pb] element 4 r + q: pair pb*32 + 8 r + 4 half + q, weight row r0 + l32
+        if (r0 + l32 < n) {
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int p = pb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                    if (p < np) {
+                        const float v = acc[pb][i] * gmul;
+                        const int64_t o = qid[p] * n + r0 + l32;
+                        if (y_bf16) reinterpret_cast<uint16_t*>(yv)[o] = f32_to_bf16_rne(v);
+                        else reinterpret_cast<float*>(yv)[o] = v;
+                    }
+                }
+        }
+    }
+}
+
+template <int FMT>
+static void launch_moe_gemm_stream(const MoeGemmArgs& a, const int32_t* goff, const int32_t* gperm, hipStream_t st) {
+    const int64_t tiles = (a.n + kMgRows - 1) / kMgRows;
+    hipLaunchKernelGGL(moe_gemm_stream_kernel<FMT>, dim3((unsigned)tiles, (unsigned)a.experts), dim3(512), 0, st,
+                       a.codes, a.scales, a.gscale, goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y,
+                       a.y_bf16, a.n, a.k);
+}
+
+// The register-resident kernel runs MXFP8 and NVFP4 rows of an odd number of
+// 16-element blocks (8-byte rows); everything else takes the streaming kernel.
 template <int FMT, int KS, int MB>
 static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const int32_t* gperm, hipStream_t st) {
     constexpr int ROWS = kMoeGemmWaves / KS * 16;
     const int64_t tiles = (a.n + ROWS - 1) / ROWS;
     static_assert(kPairsPerBlock == 16, "moe_gemm_x_lds assumes blocks of 16 pairs");
-    const dim3 grid((unsigned)tiles, (unsigned)a.experts);
-    if (FMT == kNVFP4 && a.k % 32 != 0)
-        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), grid, dim3(kMoeGemmWaves * 64),
-                           (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff, gperm, a.x,
-                           a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
-    else
-        hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, false>), grid, dim3(kMoeGemmWaves * 64),
-                           (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff, gperm, a.x,
-                           a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
+    hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), dim3((unsigned)tiles, (unsigned)a.experts),
+                       dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff,
+                       gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
-// Register blocks per lane (MB) and k split (KS): the smallest capacity
+// Streaming kernel: E2M1 codes in whole 32-element blocks.  Register-resident
+// kernel, register blocks per lane (MB) and k split (KS): the smallest capacity
 // 4 * MB * KS blocks that holds the row, at most 8 blocks per lane (MI355X,
-// 30B-A3B gate/up bank, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us,
-// 4 x 4 179 us; its down bank: 1 x 6 93 us, 2 x 4 129 us).  E4M3 blocks take
-// twice the registers: at most 4 per lane (6 or 8 spill), split up to 8 ways.
+// 30B-A3B gate/up bank, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us, 4 x 4
+// 179 us; its down bank: 1 x 6 93 us, 2 x 4 129 us).  E4M3 blocks take twice
+// the registers: at most 4 per lane (6 or 8 spill), split up to 8 ways.
 template <int FMT>
 static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t pairs = a.m * a.topk;
     int32_t* goff = a.workspace;
     int32_t* gperm = a.workspace + a.experts + 1;
-    const int64_t nblk = (a.k + 31) / 32;
-    static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
-    static constexpr int kCand8[][2] = {{1, 4}, {2, 4}, {4, 4}, {8, 4}};
-    int best_ks = 0, best_mb = 0;
-    int64_t best_cap = 0;
-    auto consider = [&](int ks, int mb) {
-        const int64_t cap = 4LL * ks * mb;
-        if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = ks; best_mb = mb; best_cap = cap; }
+    auto group = [&]() {
+        hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff,
+                           gperm, a.y, a.y_bf16, a.n);
     };
-    if constexpr (FMT == kMXFP8) {
-        for (const auto& c : kCand8) consider(c[0], c[1]);
-    } else {
-        for (const auto& c : kCand4) consider(c[0], c[1]);
+    if constexpr (FMT != kMXFP8) {
+        if (a.k % 32 == 0) {
+            group();
+            launch_moe_gemm_stream<FMT>(a, goff, gperm, st);
+            return true;
+        }
     }
-    if (best_ks == 0) return false;
-    hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff, gperm,
-                       a.y, a.y_bf16, a.n);
+    if constexpr (FMT == kMXFP4) {
+        return false;  // MX rows are whole 32-element blocks
+    } else {
+        const int64_t nblk = (a.k + 31) / 32;
+        static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
+        static constexpr int kCand8[][2] = {{1, 4}, {2, 4}, {4, 4}, {8, 4}};
+        int best_ks = 0, best_mb = 0;
+        int64_t best_cap = 0;
+        auto consider = [&](int ks, int mb) {
+            const int64_t cap = 4LL * ks * mb;
+            if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = ks; best_mb = mb; best_cap = cap; }
+        };
+        if constexpr (FMT == kMXFP8) {
+            for (const auto& c : kCand8) consider(c[0], c[1]);
+        } else {
+            for (const auto& c : kCand4) consider(c[0], c[1]);
+        }
+        if (best_ks == 0) return false;
+        group();
 #define MXQ_MG_CASE(KS_, MB_) \
     if (best_ks == KS_ && best_mb == MB_) { launch_moe_gemm_ks<FMT, KS_, MB_>(a, goff, gperm, st); return true; }
-    if constexpr (FMT == kMXFP8) {
-        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(2, 4) MXQ_MG_CASE(4, 4) MXQ_MG_CASE(8, 4)
-    } else {
-        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
-        MXQ_MG_CASE(4, 8)
-    }
+        if constexpr (FMT == kMXFP8) {
+            MXQ_MG_CASE(1, 4) MXQ_MG_CASE(2, 4) MXQ_MG_CASE(4, 4) MXQ_MG_CASE(8, 4)
+        } else {
+            MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
+            MXQ_MG_CASE(4, 8)
+        }
 #undef MXQ_MG_CASE
-    return false;
+        return false;
+    }
 }
 
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st) {
