@@ -5,12 +5,13 @@
 // release" post credits its MXFP4 MoE prefill gain to kernels that work expert
 // by expert.  Kernels:
 //
+//  * moe_gemm_stream_kernel (E2M1 codes, rows of whole 32-element blocks):
+//    each workgroup finds its expert's pairs in the ids itself (in pair order)
+//    and streams the expert's weight rows through registers slice by slice
+//    against the pairs' inputs gathered into LDS (below).
 //  * moe_group_kernel groups the pairs by expert (counts, prefix sums, and a
 //    permutation of the pairs) in a caller workspace, on the GPU, so nothing
-//    waits for the host.
-//  * moe_gemm_stream_kernel (E2M1 codes, rows of whole 32-element blocks):
-//    the expert's weight rows stream through registers slice by slice against
-//    its pairs' inputs gathered into LDS (below).
+//    waits for the host; the register-resident kernel reads it.
 //  * moe_gemm_kernel (E4M3 codes, and NVFP4 rows of an odd number of 16-element
 //    blocks): grid (row tile, expert).  Each wave loads its 16 weight
 //    rows (over its k range) into registers once; the workgroup then walks
@@ -20,9 +21,10 @@
 //    pairs to each expert, too few for a GEMM tile of hundreds of rows; here
 //    every weight byte is read from HBM once and decoded once per 16 pairs.
 //
-// The order of pairs inside a group follows atomic increments; each output
-// value is computed by the same arithmetic wherever its pair sits in a block,
-// so results are identical run to run.  A pair whose id is outside [0, E) gets
+// The grouping kernel orders an expert's pairs by atomic increments, the
+// streaming kernel by pair index; each output value is computed by the same
+// arithmetic wherever its pair sits in a block, so results are identical run
+// to run.  A pair whose id is outside [0, E) gets
 // a NaN output row.
 #include "block_operand.hpp"
 #include "gemv_mfma.hpp"
@@ -321,18 +323,16 @@ constexpr int kMgXStride = kMgBK + 8;  // bf16 per LDS row (16-byte pad: 16 rows
 template <int FMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_stream_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
-    const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
+    const int32_t* __restrict__ ids, int64_t pairs, int64_t experts, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
     static_assert(FMT != kMXFP8, "E2M1 codes: one 16-byte block per lane and slice");
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kMgPairs * kMgXStride];
     __shared__ int64_t xrow[kMgPairs];  // input row of each pair of the pass, -1 past its end
     __shared__ int64_t qid[kMgPairs];   // output row (pair index) of each pair of the pass
+    __shared__ int32_t wcnt[8];         // matches per wave in the chunk being scanned
+    __shared__ int64_t s_next;          // where the next pass's scan starts, when a chunk overflows the pass
 
     const int64_t e = blockIdx.y;
-    const int64_t c0 = goff[e];
-    const int64_t cnt = goff[e + 1] - c0;
-    if (cnt <= 0) return;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
@@ -345,15 +345,94 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
     const int64_t nk = (k + kMgBK - 1) / kMgBK;
     const int gp = tid >> 3, gc = tid & 7;  // gather: pair gp, columns 8 gc .. 8 gc + 7 of the slice
+    const uint64_t below = (uint64_t(1) << lane) - 1;
 
+    // The expert's pairs, in pair order, 64 per pass, found by scanning the ids
+    // (no separate grouping launch): each thread loads 8 ids at once, chunk j of
+    // 512 consecutive pairs is compacted by wave ballots and a per-wave prefix.
+    // The scan resumes where the previous pass stopped.  Workgroups of expert 0
+    // also write NaN to their 256 columns of every pair with an invalid id.
+    constexpr int kScanIds = 8;
+    int64_t pos = 0;  // workgroup uniform
     using Frag = WFrag<FMT, 32>;
-    for (int64_t p0 = 0; p0 < cnt; p0 += kMgPairs) {
-        const int np = (int)(cnt - p0 < kMgPairs ? cnt - p0 : kMgPairs);
+    // this lane's block of slice s (cached loads: the other blocks of each 128-byte
+    // line come with the next slices); past k, zero codes and a unit scale are
+    // selected when the block is decoded
+    auto load_w = [&](int64_t s, Frag& f) {
+        const int64_t kb = s * kMgBK + half * 32;
+        const int64_t kc = kb < k ? kb : 0;
+        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kc / 2);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) f.w[d] = v[d];
+        if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
+        else f.s = srow[kc / 32];
+    };
+    auto live = [&](int64_t s, const Frag& f) {
+        const bool ok = s * kMgBK + half * 32 < k;
+        Frag g;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) g.w[d] = ok ? f.w[d] : 0u;
+        g.s = ok ? f.s : (FMT == kNVFP4 ? 0x3838u : 127u);
+        return g;
+    };
+    for (;;) {
+        // the first slices' codes are requested before the scan (they do not depend on it)
+        Frag ring[kMgDepthW];
+        static_for<0, kMgDepthW>([&](auto J) { load_w(J, ring[J]); });
         __syncthreads();  // the previous pass is done with xrow, qid and xs
-        if (tid < kMgPairs) {
-            const int64_t q = tid < np ? gperm[c0 + p0 + tid] : -1;
-            qid[tid] = q;
-            xrow[tid] = q >= 0 ? q / xdiv : -1;
+        int found = 0;
+        while (found < kMgPairs && pos < pairs) {
+            int32_t id[kScanIds];
+#pragma unroll
+            for (int j = 0; j < kScanIds; ++j) {
+                const int64_t q = pos + 512 * j + tid;
+                id[j] = q < pairs ? ids[q] : (int32_t)experts;  // past the end: matches no expert
+            }
+            bool full = false;
+#pragma unroll
+            for (int j = 0; j < kScanIds; ++j) {
+                const int64_t q = pos + 512 * j + tid;
+                const bool hit = id[j] == (int32_t)e;
+                if (e == 0 && q < pairs && (id[j] < 0 || id[j] >= (int32_t)experts)) {
+                    for (int c = 0; c < kMgRows; ++c) {
+                        const int64_t col = (int64_t)blockIdx.x * kMgRows + c;
+                        if (col < n) {
+                            if (y_bf16) reinterpret_cast<uint16_t*>(yv)[q * n + col] = 0x7FC0u;
+                            else reinterpret_cast<float*>(yv)[q * n + col] = __builtin_nanf("");
+                        }
+                    }
+                }
+                const uint64_t mask = __ballot(hit);
+                if (lane == 0) wcnt[wave] = __popcll(mask);
+                __syncthreads();
+                int base = found, tot = 0;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    base += w < wave ? wcnt[w] : 0;
+                    tot += wcnt[w];
+                }
+                const int idx = base + __popcll(mask & below);
+                if (hit && idx < kMgPairs) {
+                    qid[idx] = q;
+                    xrow[idx] = q / xdiv;
+                }
+                if (hit && idx == kMgPairs) s_next = q;  // the first pair of the next pass
+                __syncthreads();
+                if (found + tot >= kMgPairs) {  // the pass is full (uniform)
+                    pos = found + tot > kMgPairs ? s_next : pos + 512 * (j + 1);
+                    found = kMgPairs;
+                    full = true;
+                    break;
+                }
+                found += tot;
+            }
+            if (!full) pos += 512 * kScanIds;
+        }
+        if (found == 0) break;
+        const int np = found;
+        if (tid < kMgPairs && tid >= np) {
+            qid[tid] = -1;
+            xrow[tid] = -1;
         }
         __syncthreads();
         const int64_t xr = xrow[gp];
@@ -370,31 +449,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
             const bool ok = xr >= 0 && k0 + 8 * gc < k;
             *reinterpret_cast<u32x4g_t*>(&xs[buf][gp * kMgXStride + 8 * gc]) = ok ? v : u32x4g_t{0u, 0u, 0u, 0u};
         };
-        // this lane's block of slice s (cached loads: the other blocks of each 128-byte
-        // line come with the next slices); past k, zero codes and a unit scale are
-        // selected when the block is decoded
-        auto load_w = [&](int64_t s, Frag& f) {
-            const int64_t kb = s * kMgBK + half * 32;
-            const int64_t kc = kb < k ? kb : 0;
-            const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kc / 2);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) f.w[d] = v[d];
-            if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
-            else f.s = srow[kc / 32];
-        };
-        auto live = [&](int64_t s, const Frag& f) {
-            const bool ok = s * kMgBK + half * 32 < k;
-            Frag g;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) g.w[d] = ok ? f.w[d] : 0u;
-            g.s = ok ? f.s : (FMT == kNVFP4 ? 0x3838u : 127u);
-            return g;
-        };
         // the rings: slice j's codes in ring[j % kMgDepthW]; its gathered inputs in
         // xq[j % kMgDepthX] until stored to LDS at the end of slice j - 1.  Slices are
         // taken kMgDepthX at a time; those past the last one multiply zeros.
-        Frag ring[kMgDepthW];
-        static_for<0, kMgDepthW>([&](auto J) { load_w(J, ring[J]); });
         u32x4g_t xq[kMgDepthX];
         put(0, 0, gather(0));
         static_for<1, kMgDepthX>([&](auto J) { xq[J] = gather((int64_t)J * kMgBK); });
@@ -447,11 +504,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
 }
 
 template <int FMT>
-static void launch_moe_gemm_stream(const MoeGemmArgs& a, const int32_t* goff, const int32_t* gperm, hipStream_t st) {
+static void launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t tiles = (a.n + kMgRows - 1) / kMgRows;
     hipLaunchKernelGGL(moe_gemm_stream_kernel<FMT>, dim3((unsigned)tiles, (unsigned)a.experts), dim3(512), 0, st,
-                       a.codes, a.scales, a.gscale, goff, gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y,
-                       a.y_bf16, a.n, a.k);
+                       a.codes, a.scales, a.gscale, a.ids, a.m * a.topk, a.experts, a.x,
+                       a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
 // The register-resident kernel runs MXFP8 and NVFP4 rows of an odd number of
@@ -483,8 +540,7 @@ static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     };
     if constexpr (FMT != kMXFP8) {
         if (a.k % 32 == 0) {
-            group();
-            launch_moe_gemm_stream<FMT>(a, goff, gperm, st);
+            launch_moe_gemm_stream<FMT>(a, st);
             return true;
         }
     }
