@@ -332,13 +332,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     __shared__ int32_t wcnt[8];         // matches per wave in the chunk being scanned
     __shared__ int64_t s_next;          // where the next pass's scan starts, when a chunk overflows the pass
 
-    const int64_t e = blockIdx.y;
+    // Workgroups are dealt to the 8 XCDs in turn by linear id; when the experts
+    // divide evenly, all tiles of an expert go to one XCD so that its pairs'
+    // inputs are fetched into one L2.
+    int64_t e = blockIdx.y, tile = blockIdx.x;
+    if (experts % 8 == 0) {
+        const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const int64_t j = lin / 8;
+        e = lin % 8 + 8 * (j / gridDim.x);
+        tile = j % gridDim.x;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     const int64_t rowbytes = code_bytes_per_row(FMT, k);
     const int64_t sbytes = k / block_elems(FMT);
-    const int64_t r0 = (int64_t)blockIdx.x * kMgRows + wave * 32;
+    const int64_t r0 = tile * kMgRows + wave * 32;
     const int64_t wrow = r0 + l32 < n ? r0 + l32 : n - 1;
     const uint8_t* crow = codes + (e * n + wrow) * rowbytes;
     const uint8_t* srow = scales + (e * n + wrow) * sbytes;
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
                 const bool hit = id[j] == (int32_t)e;
                 if (e == 0 && q < pairs && (id[j] < 0 || id[j] >= (int32_t)experts)) {
                     for (int c = 0; c < kMgRows; ++c) {
-                        const int64_t col = (int64_t)blockIdx.x * kMgRows + c;
+                        const int64_t col = tile * kMgRows + c;
                         if (col < n) {
                             if (y_bf16) reinterpret_cast<uint16_t*>(yv)[q * n + col] = 0x7FC0u;
                             else reinterpret_cast<float*>(yv)[q * n + col] = __builtin_nanf("");
