@@ -74,6 +74,26 @@ def test_one_expert_takes_several_row_tiles(fmt):
 
 
 @pytest.mark.parametrize("fmt", [1, 3])
+@pytest.mark.parametrize("E,per", [(16, 0), (12, 1)])
+def test_pair_scan_across_chunks(fmt, E, per):
+    """4400 pairs: more than one 4096-pair scan chunk.  Slot 0 of most tokens
+    routes to expert 0, so its ~900 pairs take 15 passes whose boundaries fall
+    inside chunks and across the chunk boundary; 16 experts take the XCD-grouped
+    workgroup order, 12 the plain one.  Every output checked."""
+    m, topk = 1100, 4
+    _, _, _, si, _ = synth.streams(150 + E + fmt)
+    ids = synth.moe_ids(si, m, topk, E)
+    rng = np.random.default_rng(E + fmt)
+    for t in np.flatnonzero(rng.random(m) < 0.8):
+        row = ids[t]
+        if 0 in row:  # keep the token's experts distinct: swap expert 0 into slot 0
+            row[np.flatnonzero(row == 0)[0]] = row[0]
+        row[0] = 0
+    c = case(fmt, E, 72, 96, m, topk, 160 + E + fmt, per, ids=ids)
+    check(c, f"pair scan across chunks {FMT_NAMES[fmt]} E={E} per_slot={per}")
+
+
+@pytest.mark.parametrize("fmt", [1, 3])
 def test_bf16_output_is_rne_of_fp32(fmt):
     c = case(fmt, 16, 300, 512, 70, 4, 90 + fmt)
     say("moe gemm bf16 epilogue", fmt)
