@@ -5,15 +5,16 @@
 // release" post credits its MXFP4 MoE prefill gain to kernels that work expert
 // by expert.  Kernels:
 //
-//  * moe_gemm_stream_kernel (E2M1 codes, rows of whole 32-element blocks):
+//  * moe_gemm_stream_kernel (rows of whole 32-element blocks, every format):
 //    each workgroup finds its expert's pairs in the ids itself (in pair order)
 //    and streams the expert's weight rows through registers slice by slice
 //    against the pairs' inputs gathered into LDS (below).
 //  * moe_group_kernel groups the pairs by expert (counts, prefix sums, and a
 //    permutation of the pairs) in a caller workspace, on the GPU, so nothing
 //    waits for the host; the register-resident kernel reads it.
-//  * moe_gemm_kernel (E4M3 codes, and NVFP4 rows of an odd number of 16-element
-//    blocks): grid (row tile, expert).  Each wave loads its 16 weight
+//  * moe_gemm_kernel (NVFP4 rows of an odd number of 16-element blocks, whose
+//    8-byte rows the streaming kernel's 16-byte loads do not fit): grid (row
+//    tile, expert).  Each wave loads its 16 weight
 //    rows (over its k range) into registers once; the workgroup then walks
 //    the expert's pairs in blocks of 16, gathers their input rows into LDS and
 //    runs 16 x 16 x 32 bf16 MFMAs with the 16 pairs as the B operand's columns
@@ -301,11 +302,11 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
 // Grid (tile of 256 weight rows, expert).  Wave w owns weight rows tile*256 +
 // 32w .. +31, one 32-row block of 32x32x16 bf16 MFMAs (the B operand's
 // columns); the expert's pairs are taken 64 at a time, two 32-pair blocks as
-// the A operand's rows.  Per 64-wide k slice the workgroup gathers the 64
-// pairs' inputs into LDS (double buffered; one 16-byte piece per thread) and
-// every wave multiplies them with its rows' codes, decoded to bf16 in
-// registers; lane (l32, h) holds the 32-element block h of the slice of its
-// row l32 (the k order of gemm.hip).  Codes and gathered inputs stream through
+// the A operand's rows.  Per k slice (64 wide, 32 for E4M3) the workgroup
+// gathers the 64 pairs' inputs into LDS (double buffered; one 16- or 8-byte
+// piece per thread) and every wave multiplies them with its rows' codes,
+// decoded to bf16 in registers; lane (l32, h) holds the 16 bytes of codes of
+// half h of the slice of its row l32 (the k order of gemm.hip).  Codes and gathered inputs stream through
 // rings of slices in registers, each slot refilled as soon as it is used, so
 // a wave keeps loads in flight from start to end, as the GEMV engine does; the register-resident kernel above instead
 // loads its whole tile first and then computes, and two such workgroups per
@@ -316,16 +317,27 @@ typedef float f32x16m_t __attribute__((ext_vector_type(16)));
 // 30B-A3B banks, 512 tokens x top-8, MXFP4 gate/up / down: 92 / 53 us with two
 // of each (NVFP4 110 / 59); inputs four ahead 92 / 53 (NVFP4 115 / 59); with
 // inputs one ahead, and before the loop's branches and full waits went, 129 / 55.
-constexpr int kMgRows = 256, kMgPairs = 64, kMgBK = 64, kMgDepthW = 2, kMgDepthX = 2;
+constexpr int kMgRows = 256, kMgPairs = 64, kMgDepthW = 2, kMgDepthX = 2;
 static_assert(kMgDepthX % kMgDepthW == 0, "the unrolled loop indexes both rings statically");
-constexpr int kMgXStride = kMgBK + 8;  // bf16 per LDS row (16-byte pad: 16 rows' reads hit distinct banks)
+// Slice shape: 64 k (each lane's share of a row one 32-element block, 16 bytes of
+// E2M1 codes), or 32 k for E4M3 (a 16-element half block, 16 bytes, as gemm.hip).
+template <int FMT>
+struct MgSlice {
+    static constexpr int BK = FMT == kMXFP8 ? 32 : 64;
+    static constexpr int KE = BK / 2;     // k per lane and slice
+    static constexpr int STEPS = BK / 16; // MFMA k steps per slice
+    static constexpr int XS = BK + 8;     // bf16 per LDS row (16-byte pad: 16 rows' reads hit distinct banks)
+    static constexpr int EPT = BK / 8;    // gathered input elements per thread and slice (64 pairs, 512 threads)
+};
 
 template <int FMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_stream_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ ids, int64_t pairs, int64_t experts, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
-    static_assert(FMT != kMXFP8, "E2M1 codes: one 16-byte block per lane and slice");
+    using MS = MgSlice<FMT>;
+    constexpr int kMgBK = MS::BK, kMgXStride = MS::XS, KE = MS::KE, EPT = MS::EPT;
+    using XPiece = std::conditional_t<EPT == 8, u32x4g_t, u32x2g_t>;
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kMgPairs * kMgXStride];
     __shared__ int64_t xrow[kMgPairs];  // input row of each pair of the pass, -1 past its end
     __shared__ int64_t qid[kMgPairs];   // output row (pair index) of each pair of the pass
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     const uint8_t* srow = scales + (e * n + wrow) * sbytes;
     const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
     const int64_t nk = (k + kMgBK - 1) / kMgBK;
-    const int gp = tid >> 3, gc = tid & 7;  // gather: pair gp, columns 8 gc .. 8 gc + 7 of the slice
+    const int gp = tid >> 3, gc = tid & 7;  // gather: pair gp, columns EPT gc .. EPT gc + EPT - 1 of the slice
     const uint64_t below = (uint64_t(1) << lane) - 1;
 
     // The expert's pairs, in pair order, 64 per pass, found by scanning the ids
@@ -363,21 +375,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     // also write NaN to their 256 columns of every pair with an invalid id.
     constexpr int kScanIds = 8;
     int64_t pos = 0;  // workgroup uniform
-    using Frag = WFrag<FMT, 32>;
+    using Frag = WFrag<FMT, KE>;
     // this lane's block of slice s (cached loads: the other blocks of each 128-byte
     // line come with the next slices); past k, zero codes and a unit scale are
     // selected when the block is decoded
     auto load_w = [&](int64_t s, Frag& f) {
-        const int64_t kb = s * kMgBK + half * 32;
+        const int64_t kb = s * kMgBK + half * KE;
         const int64_t kc = kb < k ? kb : 0;
-        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + kc / 2);
+        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + (FMT == kMXFP8 ? kc : kc / 2));
 #pragma unroll
         for (int d = 0; d < 4; ++d) f.w[d] = v[d];
         if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
         else f.s = srow[kc / 32];
     };
     auto live = [&](int64_t s, const Frag& f) {
-        const bool ok = s * kMgBK + half * 32 < k;
+        const bool ok = s * kMgBK + half * KE < k;
         Frag g;
 #pragma unroll
         for (int d = 0; d < 4; ++d) g.w[d] = ok ? f.w[d] : 0u;
@@ -450,18 +462,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
         // every load in flight): addresses clamped into the tensors, the values
         // selected away past k or past the pass's pairs only where they are used.
         auto gather = [&](int64_t k0) {
-            const int64_t kk = k0 + 8 * gc;
+            const int64_t kk = k0 + EPT * gc;
             const bool ok = xr >= 0 && kk < k;
-            return *reinterpret_cast<const u32x4g_t*>(x + (ok ? xr * k + kk : 0));
+            return *reinterpret_cast<const XPiece*>(x + (ok ? xr * k + kk : 0));
         };
-        auto put = [&](int buf, int64_t k0, const u32x4g_t& v) {  // v = gather(k0)
-            const bool ok = xr >= 0 && k0 + 8 * gc < k;
-            *reinterpret_cast<u32x4g_t*>(&xs[buf][gp * kMgXStride + 8 * gc]) = ok ? v : u32x4g_t{0u, 0u, 0u, 0u};
+        auto put = [&](int buf, int64_t k0, const XPiece& v) {  // v = gather(k0)
+            const bool ok = xr >= 0 && k0 + EPT * gc < k;
+            *reinterpret_cast<XPiece*>(&xs[buf][gp * kMgXStride + EPT * gc]) = ok ? v : XPiece{};
         };
         // the rings: slice j's codes in ring[j % kMgDepthW]; its gathered inputs in
         // xq[j % kMgDepthX] until stored to LDS at the end of slice j - 1.  Slices are
         // taken kMgDepthX at a time; those past the last one multiply zeros.
-        u32x4g_t xq[kMgDepthX];
+        XPiece xq[kMgDepthX];
         put(0, 0, gather(0));
         static_for<1, kMgDepthX>([&](auto J) { xq[J] = gather((int64_t)J * kMgBK); });
         // barriers wait for LDS traffic only (__syncthreads would also wait for every
@@ -478,17 +490,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
                 const int64_t s = s0 + J;
                 constexpr int JW = decltype(J)::value % kMgDepthW;
                 xq[J] = gather((s + kMgDepthX) * kMgBK);
-                const uint16_t* as = &xs[s & 1][l32 * kMgXStride + half * 32];
-                const Frag w = live(s, ring[JW]);
-                static_for<0, 4>([&](auto S) {
-                    const bf16x8_t b = decode_step<FMT, decltype(S)::value>(w);
-                    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(as + S * 8);
-                    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
-                    if (two) {
-                        const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(as + 32 * kMgXStride + S * 8);
-                        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+                const uint16_t* as = &xs[s & 1][l32 * kMgXStride + half * KE];
+                Frag w = live(s, ring[JW]);
+                auto mfmas = [&]() {
+                    static_for<0, MS::STEPS>([&](auto S) {
+                        const bf16x8_t b = decode_step<FMT, decltype(S)::value>(w);
+                        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(as + S * 8);
+                        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+                        if (two) {
+                            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(as + 32 * kMgXStride + S * 8);
+                            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+                        }
+                    });
+                };
+                if constexpr (FMT != kMXFP8) {
+                    mfmas();
+                } else {
+                    // E4M3 blocks with an E8M0 byte below kMx8Lift (rare; the branch is
+                    // wave uniform): first the other fragments, then the lifted ones,
+                    // decoded 2^kMx8Lift larger, against the inputs scaled by 2^-kMx8Lift
+                    // (exact in bf16 down to inputs whose products with such weights lie
+                    // below the fp32 subnormals).
+                    const bool lifted = __ballot(frag_lifted(w)) != 0;
+                    if (lifted) {
+                        const bool lo = frag_lifted(w);
+#pragma unroll
+                        for (int d = 0; d < Frag::DW; ++d) w.w[d] = lo ? 0u : w.w[d];
                     }
-                });
+                    mfmas();
+                    if (lifted) {
+                        w = live(s, ring[JW]);
+                        const bool lo = frag_lifted(w);
+#pragma unroll
+                        for (int d = 0; d < Frag::DW; ++d) w.w[d] = lo ? w.w[d] : 0u;
+                        w.s = lo ? w.s + kMx8Lift : 127u;
+                        // 8 bf16 times 2^-kMx8Lift: the exponent field lowered; inputs below
+                        // 2^-123 become zeros of their sign (their products with these weights
+                        // are far below the fp32 subnormals), infinities and NaNs stay
+                        auto down = [](const uint16_t* p) {
+                            const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(p);
+                            u32x4g_t r;
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) {
+                                uint32_t o = 0u;
+#pragma unroll
+                                for (int hh = 0; hh < 2; ++hh) {
+                                    const uint32_t h = (v[d] >> (16 * hh)) & 0xFFFFu;
+                                    const uint32_t e = (h >> 7) & 0xFFu;
+                                    const uint32_t q = e == 0xFFu ? h : (e > kMx8Lift ? h - (kMx8Lift << 7) : (h & 0x8000u));
+                                    o |= q << (16 * hh);
+                                }
+                                r[d] = o;
+                            }
+                            return __builtin_bit_cast(bf16x8_t, r);
+                        };
+                        static_for<0, MS::STEPS>([&](auto S) {
+                            const bf16x8_t b = decode_step<FMT, decltype(S)::value>(w);
+                            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(down(as + S * 8), b, acc[0], 0, 0, 0);
+                            if (two)
+                                acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(down(as + 32 * kMgXStride + S * 8), b,
+                                                                                 acc[1], 0, 0, 0);
+                        });
+                    }
+                }
                 load_w(s + kMgDepthW, ring[JW]);
                 put((int)((s + 1) & 1), (s + 1) * kMgBK, xq[(decltype(J)::value + 1) % kMgDepthX]);
                 lds_barrier();
@@ -520,8 +584,8 @@ static void launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t st) {
                        a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
-// The register-resident kernel runs MXFP8 and NVFP4 rows of an odd number of
-// 16-element blocks (8-byte rows); everything else takes the streaming kernel.
+// The register-resident kernel runs NVFP4 rows of an odd number of 16-element
+// blocks (8-byte rows); everything else takes the streaming kernel.
 template <int FMT, int KS, int MB>
 static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const int32_t* gperm, hipStream_t st) {
     constexpr int ROWS = kMoeGemmWaves / KS * 16;
@@ -532,12 +596,12 @@ static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const 
                        gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
 }
 
-// Streaming kernel: E2M1 codes in whole 32-element blocks.  Register-resident
-// kernel, register blocks per lane (MB) and k split (KS): the smallest capacity
-// 4 * MB * KS blocks that holds the row, at most 8 blocks per lane (MI355X,
-// 30B-A3B gate/up bank, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us, 4 x 4
-// 179 us; its down bank: 1 x 6 93 us, 2 x 4 129 us).  E4M3 blocks take twice
-// the registers: at most 4 per lane (6 or 8 spill), split up to 8 ways.
+// Streaming kernel: rows of whole 32-element blocks (every MX row; NVFP4 with
+// k % 32 == 0).  Register-resident kernel (the other NVFP4 rows), register
+// blocks per lane (MB) and k split (KS): the smallest capacity 4 * MB * KS
+// blocks that holds the row, at most 8 blocks per lane (MI355X, 30B-A3B gate/up
+// bank in MXFP4, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us, 4 x 4 179 us;
+// its down bank: 1 x 6 93 us, 2 x 4 129 us).
 template <int FMT>
 static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t pairs = a.m * a.topk;
@@ -547,39 +611,28 @@ static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff,
                            gperm, a.y, a.y_bf16, a.n);
     };
-    if constexpr (FMT != kMXFP8) {
-        if (a.k % 32 == 0) {
-            launch_moe_gemm_stream<FMT>(a, st);
-            return true;
-        }
+    if (a.k % 32 == 0) {
+        launch_moe_gemm_stream<FMT>(a, st);
+        return true;
     }
-    if constexpr (FMT == kMXFP4) {
+    if constexpr (FMT != kNVFP4) {
         return false;  // MX rows are whole 32-element blocks
     } else {
         const int64_t nblk = (a.k + 31) / 32;
         static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
-        static constexpr int kCand8[][2] = {{1, 4}, {2, 4}, {4, 4}, {8, 4}};
         int best_ks = 0, best_mb = 0;
         int64_t best_cap = 0;
         auto consider = [&](int ks, int mb) {
             const int64_t cap = 4LL * ks * mb;
             if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = ks; best_mb = mb; best_cap = cap; }
         };
-        if constexpr (FMT == kMXFP8) {
-            for (const auto& c : kCand8) consider(c[0], c[1]);
-        } else {
-            for (const auto& c : kCand4) consider(c[0], c[1]);
-        }
+        for (const auto& c : kCand4) consider(c[0], c[1]);
         if (best_ks == 0) return false;
         group();
 #define MXQ_MG_CASE(KS_, MB_) \
     if (best_ks == KS_ && best_mb == MB_) { launch_moe_gemm_ks<FMT, KS_, MB_>(a, goff, gperm, st); return true; }
-        if constexpr (FMT == kMXFP8) {
-            MXQ_MG_CASE(1, 4) MXQ_MG_CASE(2, 4) MXQ_MG_CASE(4, 4) MXQ_MG_CASE(8, 4)
-        } else {
-            MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
-            MXQ_MG_CASE(4, 8)
-        }
+        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
+        MXQ_MG_CASE(4, 8)
 #undef MXQ_MG_CASE
         return false;
     }

@@ -299,11 +299,11 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  * processes the tokens expert by expert for its MXFP4 MoE prefill gain; here
  * the routed (token, slot) pairs are grouped by expert on the GPU and each
  * expert's weights are decoded to bf16 and multiplied on the matrix unit with
- * its pairs' inputs (fp32 accumulate): for E2M1 codes in whole 32-element
- * blocks (MXFP4, NVFP4 with k % 32 == 0) one kernel streams each expert's rows
- * against 64 of its pairs at a time, finding them in the ids itself; MXFP8 and
- * NVFP4 rows of an odd number of 16-element blocks are grouped by a first
- * kernel into the workspace, then multiplied 16 pairs at a time:
+ * its pairs' inputs (fp32 accumulate): for rows of whole 32-element blocks
+ * (MXFP4, MXFP8, NVFP4 with k % 32 == 0) one kernel streams each expert's rows
+ * against 64 of its pairs at a time, finding them in the ids itself; NVFP4
+ * rows of an odd number of 16-element blocks are grouped by a first kernel
+ * into the workspace, then multiplied 16 pairs at a time:
  *
  *   y[t][s][i] = sum_k W[expert_ids[t][s]][i][k] * x_ts[k]
  *   x_ts = x[t] (x_per_slot == 0, e.g. gate/up) or x[t][s] (x_per_slot != 0, e.g. down)

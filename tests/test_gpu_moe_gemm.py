@@ -63,7 +63,7 @@ def test_nvfp4_rows_of_an_odd_number_of_blocks(E, n, k, m, topk, per):
     check(c, f"moe gemm nvfp4 half-block rows E={E} n={n} k={k} m={m} topk={topk} per_slot={per}")
 
 
-@pytest.mark.parametrize("fmt", [1, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_one_expert_takes_several_row_tiles(fmt):
     """Every token routes to experts 0..3: expert 0 gets 600 pairs (three 256-row
     tiles, the last ragged), the other experts of the bank none."""
@@ -73,7 +73,7 @@ def test_one_expert_takes_several_row_tiles(fmt):
     check(c, f"skewed routing {FMT_NAMES[fmt]}")
 
 
-@pytest.mark.parametrize("fmt", [1, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("E,per", [(16, 0), (12, 1)])
 def test_pair_scan_across_chunks(fmt, E, per):
     """4400 pairs: more than one 4096-pair scan chunk.  Slot 0 of most tokens
@@ -93,7 +93,7 @@ def test_pair_scan_across_chunks(fmt, E, per):
     check(c, f"pair scan across chunks {FMT_NAMES[fmt]} E={E} per_slot={per}")
 
 
-@pytest.mark.parametrize("fmt", [1, 3])
+@pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_bf16_output_is_rne_of_fp32(fmt):
     c = case(fmt, 16, 300, 512, 70, 4, 90 + fmt)
     say("moe gemm bf16 epilogue", fmt)
@@ -142,24 +142,50 @@ def test_deterministic():
         assert (host(run(c)).view(np.uint32) == y1.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_30b_a3b_prefill_sampled(which):
+def test_30b_a3b_prefill_sampled(fmt, which):
     """The 30B-A3B-like bank (128 experts; gate/up 1536 x 2048, down 2048 x 768,
     per-slot inputs) with 512 tokens x top-8 (a 512-token prompt); the oracle
     checks 24 seeded tokens (all 8 slots, every output) of the full launch."""
     n, k = synth.MOE_SHAPES[which]
     per = 1 if which == "down" else 0
-    c = case(1, 128, n, k, 512, 8, 131 if per else 130, per)
+    c = case(fmt, 128, n, k, 512, 8, (131 if per else 130) + 10 * (fmt - 1), per)
     rows = np.sort(np.random.default_rng(5).choice(512, 24, replace=False))
-    check(c, f"30B-A3B {which} prefill, 512 tokens", rows)
+    check(c, f"30B-A3B {which} prefill {FMT_NAMES[fmt]}, 512 tokens", rows)
+
+
+@pytest.mark.parametrize("per", [0, 1])
+def test_mxfp8_lifted_blocks_among_others(per):
+    """MXFP8 blocks with E8M0 bytes 0..2 (decoded 2^3 larger against inputs
+    scaled by 2^-3) scattered among ordinary blocks, some rows holding both in
+    one slice, next to blocks of large scales; every output checked."""
+    c = case(2, 8, 96, 320, 40, 4, 180 + per, per)
+    rng = np.random.default_rng(7 + per)
+    sc = c["scales"].copy()
+    pick = rng.random(sc.shape)
+    sc[pick < 0.15] = rng.integers(0, 3, size=int((pick < 0.15).sum()))
+    sc[(pick >= 0.15) & (pick < 0.2)] = 200
+    c["scales"] = sc
+    check(c, f"mxfp8 lifted blocks per_slot={per}")
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 @pytest.mark.parametrize("k", [32, 96, 768, 1024, 1280, 2048, 2560, 3072, 4064])
-def test_register_tile_variants(fmt, k):
-    """Row lengths that select every (k split, register blocks per lane) variant
-    of the per-expert kernel -- 1 x 4 (k <= 512), 1 x 6 (768), 1 x 8 (1024),
-    2 x 6 (1280), 2 x 8 (2048), 4 x 6 (2560, 3072), 4 x 8 (4064) -- including
-    ranges that end inside a lane's blocks; every output checked."""
+def test_streaming_kernel_across_k(fmt, k):
+    """Rows of whole 32-element blocks take the streaming kernel in every format:
+    one slice or many, MXFP8's 32-wide slices and the others' 64-wide ones
+    ending inside the last slice; every output checked."""
     c = case(fmt, 8, 40, k, 21, 3, 140 + k + fmt)
-    check(c, f"moe gemm variants {FMT_NAMES[fmt]} k={k}")
+    check(c, f"moe gemm streaming {FMT_NAMES[fmt]} k={k}")
+
+
+@pytest.mark.parametrize("k", [16, 48, 496, 752, 1008, 1520, 2032, 3056, 4080])
+def test_register_tile_variants(k):
+    """NVFP4 rows of an odd number of 16-element blocks take the per-expert
+    register-resident kernel; these lengths select every (k split, register
+    blocks per lane) variant -- 1 x 4 (up to 16 blocks of 32), 1 x 6 (24),
+    1 x 8 (32), 2 x 6 (48), 2 x 8 (64), 4 x 6 (96), 4 x 8 (128) -- each with
+    the row's last block half; every output checked."""
+    c = case(3, 8, 40, k, 21, 3, 170 + k)
+    check(c, f"moe gemm register variants nvfp4 k={k}")
