@@ -200,7 +200,7 @@ MXQ_API mxq_status_t mxq_gemm(mxq_format_t fmt, const uint8_t* codes, const uint
         }
         return MXQ_OK;
     }
-    const mxq::GemmArgs a{fmt, codes, scales, global_scale, x, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k};
+    const mxq::GemmArgs a{fmt, codes, scales, global_scale, x, y, y_dtype == MXQ_OUT_BF16 ? 1 : 0, m, n, k, cus};
     return launched(mxq::launch_gemm(a, as_stream(stream)));
 }
 

@@ -89,6 +89,7 @@ struct GemmArgs {
     void* y;
     int y_bf16;
     int64_t m, n, k;
+    int cus;  // compute units of the device
 };
 
 bool launch_gemv(const GemvArgs& a, const GemvConfig& cfg, hipStream_t st);

@@ -64,6 +64,20 @@ def test_nvfp4_rows_of_an_odd_number_of_blocks(m, n, k):
     assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_last_round_in_smaller_tiles(fmt):
+    """260 x 33357: 2 x 131 tiles of 256 x 256 leave a partly filled last round on
+    a 256-CU device (one workgroup per CU), so the last 3 tile columns (589
+    columns, ragged) run as a second launch of 128 x 128 tiles; every output."""
+    m, n, k = 260, 33357, 64
+    c = small_case(fmt, m, n, k, 400 + fmt)
+    say("gemm last round in smaller tiles", fmt)
+    Y = host(mxq.gemm(fmt, dev_u8(c["codes"]), dev_u8(c["scales"]), dev_bf16(c["x"]), dev_f32(c["g"]),
+                      out_dtype=torch.float32))
+    Y_ref, A_ref = oracle.gemm_rows(fmt, c["codes"], c["scales"], c["g"], c["x"], np.arange(m), n, k)
+    assert_within(Y, Y_ref, A_ref, f"gemm fmt={fmt} {m}x{n}x{k}")
+
+
 def test_gemm_rows_match_gemv():
     c = small_case(1, 9, 640, 1024, 12)
     say("gemm row == gemv")
