@@ -148,7 +148,9 @@ static void launch_down_inst(const MoeBlockArgs& a, hipStream_t st) {
 // by the gate/up kernel, 4 rows per lane (half the workgroups, each copying
 // its token's activations once) measure the same (MI355X, 30B-A3B block,
 // 2 and 4 tokens: 17.89 / 25.70 us with 4, 17.89 / 25.76 us with 2) and
-// one token is faster with 2 (14.74 vs 15.00 us).
+// one token is faster with 2 (14.74 vs 15.00 us); one row per lane (twice the
+// workgroups) is slower at every token count (routed block, 1 / 2 / 4 tokens:
+// 13.96 / 17.01 / 27.67 us against 13.47 / 16.48 / 26.43 us).
 template <int FMT, int CB, int G, int S>
 static void launch_down_gs(const MoeBlockArgs& a, hipStream_t st) {
     launch_down_inst<FMT, CB, G, S, 2>(a, st);
