@@ -640,7 +640,7 @@ static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
 
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st) {
     if (a.experts > kMaxGroupExperts) return false;
-    if (moe_gemm_x_lds(a.k) > kMoeGemmMaxXLds) return false;
+    if (a.k % 32 != 0 && moe_gemm_x_lds(a.k) > kMoeGemmMaxXLds) return false;  // (the staging kernel's LDS)
     switch (a.fmt) {
         case kMXFP4: return launch_moe_gemm_inst<kMXFP4>(a, st);
         case kMXFP8: return launch_moe_gemm_inst<kMXFP8>(a, st);

@@ -317,9 +317,10 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  *                  (written by the grouping kernel where it runs; otherwise
  *                  left as it was)
  *   m 1 .. 2^24 / topk;  topk 1 .. MXQ_MAX_TOPK;  num_experts 1 .. 1024;
- *   n >= 1;  k a positive multiple of the block size (32 MX, 16 NVFP4), at
- *   most 4088 (the inputs of 16 pairs are staged in 128 KiB of LDS; larger k
- *   gives MXQ_E_UNSUPPORTED)
+ *   n >= 1;  k a positive multiple of the block size (32 MX, 16 NVFP4), up
+ *   to 2^31 - 1; NVFP4 rows of an odd number of 16-element blocks at most 4088
+ *   (the inputs of 16 pairs are staged in 128 KiB of LDS; larger k gives
+ *   MXQ_E_UNSUPPORTED)
  * A pair whose id is outside [0, num_experts) gets a NaN output row.  The
  * kernels run on `stream`; the workspace must not be shared by calls that
  * overlap.

@@ -171,11 +171,12 @@ def test_mxfp8_lifted_blocks_among_others(per):
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3])
-@pytest.mark.parametrize("k", [32, 96, 768, 1024, 1280, 2048, 2560, 3072, 4064])
+@pytest.mark.parametrize("k", [32, 96, 768, 1024, 1280, 2048, 2560, 3072, 4064, 4128, 7168, 16416])
 def test_streaming_kernel_across_k(fmt, k):
     """Rows of whole 32-element blocks take the streaming kernel in every format:
     one slice or many, MXFP8's 32-wide slices and the others' 64-wide ones
-    ending inside the last slice; every output checked."""
+    ending inside the last slice, and rows longer than the staging kernel's LDS
+    allows (k > 4088); every output checked."""
     c = case(fmt, 8, 40, k, 21, 3, 140 + k + fmt)
     check(c, f"moe gemm streaming {FMT_NAMES[fmt]} k={k}")
 
