@@ -17,7 +17,8 @@ The kernels checked: the FMA GEMV at batch 1 (and forced at batch 4), the
 matrix-mode GEMV at batches 2 and 4 (and forced at batch 1), the matrix-unit
 GEMV at batch 8 (and forced at batch 1), the expert-indexed MoE GEMV (one pair per
 round at one token, two from two tokens up), the prefill GEMM on its tile path
-(m > 32) and its small-m path, and the expert-batched MoE GEMM.  The MoE decode
+(m > 32), its last-round launch of 128 x 128 tiles and its small-m path, and
+the expert-batched MoE GEMM.  The MoE decode
 block's down projection runs the FMA GEMV's decode (the same streaming engine).
 """
 import numpy as np
@@ -168,6 +169,30 @@ def test_gemm(tile, m):
     Y = host(mxq.gemm(fmt, tile["codes"], tile["scales"], dev_bf16(one_hot(cols)), tile["gdev"],
                       out_dtype=torch.float32))
     check(Y, tile["y_ref"][np.arange(m) % 8], tile["t"], f"gemm m={m}")
+
+
+def test_gemm_last_round_tiles(tile):
+    """The prefill GEMM's second launch, 128 x 128 tiles for a partly filled last
+    round of 256 x 256 tiles: the probe rows (for MXFP8 those of scale bytes 0-3,
+    127, 200, 254 and 255) sit after 65536 rows of zero weights, so a 64-row
+    product has 256 + 16 (MXFP8: + 8) tile columns and, with one 256 x 256
+    workgroup per CU on 256 CUs, the probe rows' columns are exactly the ones the
+    second launch takes.  Each output against the oracle's one-hot product."""
+    fmt = tile["fmt"]
+    codes, scales, gg = tile["host"]
+    t = tile["t"]
+    sel = np.isin(t[5], [0, 1, 2, 3, 127, 200, 254, 255]) if fmt == 2 else np.ones(tile["rows"], dtype=bool)
+    pad = 65536
+    zc = np.zeros((pad, codes.shape[1]), dtype=np.uint8)
+    zs = np.full((pad, scales.shape[1]), 0x38 if fmt == 3 else 127, dtype=np.uint8)  # unit scales
+    C, S = np.vstack([zc, codes[sel]]), np.vstack([zs, scales[sel]])
+    m = 64
+    cols = J[np.arange(m) % 8]
+    say("decode paths: gemm last round", NAMES[fmt])
+    Y = host(mxq.gemm(fmt, dev_u8(C), dev_u8(S), dev_bf16(one_hot(cols)), tile["gdev"], out_dtype=torch.float32))
+    assert (Y[:, :pad] == 0).all()
+    t_sel = t[:4] + (t[4][sel], t[5][sel], t[6][sel])
+    check(Y[:, pad:], tile["y_ref"][np.arange(m) % 8][:, sel], t_sel, "gemm last round")
 
 
 def test_moe_gemm(tile):
