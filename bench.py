@@ -491,6 +491,31 @@ def main():
         t_layer = (mg["gate_up"]["us"] + mg["down"]["us"]) * 1e-6
         mg["layer"] = dict(us=round(t_layer * 1e6, 2), prefill_tok_s=round(P / (MOE_LAYERS * t_layer), 1),
                            note=f"{P}-token prompt, expert FFN of {MOE_LAYERS} layers (gate/up + down GEMMs only)")
+        # the other formats on the same banks and routing (the same streaming kernel)
+        fm = {}
+        for fmt, name in ((mxq.MXFP8, "mxfp8"), (mxq.NVFP4, "nvfp4")):
+            fm[name] = {}
+            for which in ("gate_up", "down"):
+                case = synth.moe_layer(which, 1, seed=0, fmt=fmt)
+                codes, scales = u8(case["codes"]), u8(case["scales"])
+                g = None if case["g"] is None else torch.from_numpy(case["g"]).to(dev)
+                n, k = case["n"], case["k"]
+                _, _, sx, si, _ = synth.streams(300)
+                ids = torch.from_numpy(synth.moe_ids(si, P, 8, 128)).to(dev)
+                per = 1 if which == "down" else 0
+                x = bf(synth.bf16_normal(sx, (P, 8, k) if per else (P, k)))
+                y = torch.empty((P, 8, n), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty((128 + 1 + P * 8,), dtype=torch.int32, device=dev)
+                ms = timed_graph(lambda: mxq.moe_gemm(fmt, codes, scales, ids, x, per, global_scale=g, out=y,
+                                                      workspace=ws), 10)
+                tf = 2.0 * P * 8 * n * k / (ms * 1e-3) / 1e12
+                bank = 128 * mxq.weight_bytes(fmt, n, k)
+                fm[name][which] = dict(us=round(ms * 1e3, 2), tflops=round(tf, 1),
+                                       hbm_frac=round(bank / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+                log(f"moe gemm {name} {which} {P} tokens x top-8: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+                del codes, scales, x, y, case
+                torch.cuda.empty_cache()
+        mg["formats"] = fm
         extras["moe_prefill_gemm"] = mg
 
     # ---------------- block-float quantizer and FP8 checkpoint requantizer ----------------
