@@ -99,15 +99,16 @@ constexpr int kMoeGemmWaves = 8;    // waves per workgroup (measured on MI355X: 
 // stay within the 128 registers of two workgroups per CU (their LDS allows
 // two) except NVFP4 with eight blocks per lane, which loads its weights first
 // (MI355X, 30B-A3B gate/up bank, 512 tokens: 176 us that way, 223 us with one
-// workgroup per CU).  E4M3 blocks take twice the registers either way.
+// workgroup per CU).
 template <int FMT, int MB>
 constexpr bool moe_gemm_x_first() { return !(FMT == kNVFP4 && MB == 8); }
 
 template <int FMT, int KS, int MB, bool ROW8>
-__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kMXFP8 ? 2 : 4))) void moe_gemm_kernel(
+__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
+    static_assert(FMT == kNVFP4, "E2M1 codes with E4M3 block scales (every other row streams)");
     constexpr int NW = kMoeGemmWaves;
     constexpr int ROWS = NW / KS * 16;
     __shared__ __attribute__((aligned(16))) float red[KS > 1 ? NW * 256 : 1];
@@ -200,15 +201,6 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
         for (int d = 0; d < WFrag<FMT>::DW; ++d) w[j].w[d] = ok ? w[j].w[d] : 0u;
         w[j].s = ok ? w[j].s : (FMT == kNVFP4 ? 0x3838u : 127u);
     }
-    // MXFP8 weights with an E8M0 byte below kMx8Lift anywhere in the wave: their
-    // lifted part runs as a second pass (block_operand.hpp); uniform over the wave
-    bool lifted = false;
-    if constexpr (FMT == kMXFP8) {
-        bool lo = false;
-#pragma unroll
-        for (int j = 0; j < MB; ++j) lo = lo || frag_lifted<FMT>(w[j]);
-        lifted = __ballot(lo) != 0;
-    }
 
     for (int64_t t0 = 0; t0 < cnt; t0 += kPairsPerBlock) {
         const int batch = (int)(cnt - t0 < kPairsPerBlock ? cnt - t0 : kPairsPerBlock);
@@ -249,27 +241,10 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
             // (which would hold every block's operands in registers at once)
             if (j + 1 < MB) read_x(j + 1, vb[(j + 1) & 1]);
             const u32x4g_t(&v)[4] = vb[j & 1];
-            if constexpr (FMT == kMXFP8) {
-                // one code path: lifted blocks take part with zero codes, and a
-                // wave holding one adds their lifted part (a rare second pass)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, false>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
-                if (lifted) {
-                    f32x4m_t t = {0.f, 0.f, 0.f, 0.f};
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 0, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), t, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 1, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), t, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 2, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), t, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step_part<FMT, 3, true>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), t, 0, 0, 0);
-                    acc += t * kMx8Unlift;
-                }
-            } else {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 3>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
-            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 3>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
             asm volatile("" ::: "memory");
         }
 
