@@ -289,11 +289,8 @@ MXQ_API mxq_status_t mxq_moe_gemm(mxq_format_t fmt, const uint8_t* codes, const 
     if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(global_scale, 4) ||
         !aligned(expert_ids, 4) || !aligned(workspace, 4))
         return MXQ_E_ALIGN;
-    // (rows of an odd number of 16-element NVFP4 blocks take the kernel that stages
-    // the inputs of 16 pairs in LDS; every other row streams, at any k)
-    const bool staged = fmt == MXQ_FMT_NVFP4 && k % 32 != 0;
     if (topk > MXQ_MAX_TOPK || num_experts > mxq::kMaxGroupExperts || m * topk > (int64_t(1) << 24) ||
-        n > kMaxDim || k > kMaxDim || (staged && mxq::moe_gemm_x_lds(k) > mxq::kMoeGemmMaxXLds))
+        n > kMaxDim || k > kMaxDim)
         return MXQ_E_UNSUPPORTED;
     int cus = 0;
     if ((st = check_device(&cus)) != MXQ_OK) return st;

@@ -133,8 +133,8 @@ constexpr int64_t kMoeBlockScratchBytes = int64_t(5) << 19;
 hipError_t moe_block_scratch(float** ptr);
 
 // Expert-batched MoE GEMM: Y[q][:] = W[ids[q]] . X[q / topk] (or X[q] with
-// x_per_slot) for the pairs q = token * topk + slot; workspace = goff[experts
-// + 1] then gperm[m * topk].
+// x_per_slot) for the pairs q = token * topk + slot; workspace: the caller's
+// scratch of experts + 1 + m * topk int32 (the streaming kernel needs none).
 struct MoeGemmArgs {
     int fmt;
     const uint8_t* codes;
@@ -148,11 +148,7 @@ struct MoeGemmArgs {
     int32_t* workspace;
     int64_t experts, m, n, k, topk;
 };
-constexpr int kMaxGroupExperts = 1024;
-// LDS of the gathered inputs of one block of 16 pairs (bf16 rows padded by 8
-// elements), and its budget: k up to 4088.
-constexpr int64_t moe_gemm_x_lds(int64_t k) { return 16 * (k + 8) * 2; }
-constexpr int64_t kMoeGemmMaxXLds = 128 * 1024;
+constexpr int kMaxGroupExperts = 1024;  // experts per bank of the expert-batched GEMM
 
 // Quantizer: bf16 x[rows][k] -> codes and block scales (NVFP4: per-tensor scale gscale[0] given).
 struct QuantizeArgs {

@@ -3,276 +3,23 @@
 //
 // The "Decoding block-float formats in software" section of the "MLxcel 0.8
 // release" post credits its MXFP4 MoE prefill gain to kernels that work expert
-// by expert.  Kernels:
+// by expert.  One kernel, moe_gemm_stream_kernel, serves every format and row
+// length: each workgroup finds its expert's pairs in the ids itself (in pair
+// order) and streams the expert's weight rows through registers slice by slice
+// against the pairs' inputs gathered into LDS (below).  A prompt routes a few
+// dozen pairs to each expert, too few for a GEMM tile of hundreds of rows; here
+// every weight byte is read from HBM once per 64 pairs of its expert.
 //
-//  * moe_gemm_stream_kernel (rows of whole 32-element blocks, every format):
-//    each workgroup finds its expert's pairs in the ids itself (in pair order)
-//    and streams the expert's weight rows through registers slice by slice
-//    against the pairs' inputs gathered into LDS (below).
-//  * moe_group_kernel groups the pairs by expert (counts, prefix sums, and a
-//    permutation of the pairs) in a caller workspace, on the GPU, so nothing
-//    waits for the host; the register-resident kernel reads it.
-//  * moe_gemm_kernel (NVFP4 rows of an odd number of 16-element blocks, whose
-//    8-byte rows the streaming kernel's 16-byte loads do not fit): grid (row
-//    tile, expert).  Each wave loads its 16 weight
-//    rows (over its k range) into registers once; the workgroup then walks
-//    the expert's pairs in blocks of 16, gathers their input rows into LDS and
-//    runs 16 x 16 x 32 bf16 MFMAs with the 16 pairs as the B operand's columns
-//    (the operand layout of gemv_mfma.hpp).  A prompt routes a few dozen
-//    pairs to each expert, too few for a GEMM tile of hundreds of rows; here
-//    every weight byte is read from HBM once and decoded once per 16 pairs.
-//
-// The grouping kernel orders an expert's pairs by atomic increments, the
-// streaming kernel by pair index; each output value is computed by the same
-// arithmetic wherever its pair sits in a block, so results are identical run
-// to run.  A pair whose id is outside [0, E) gets
-// a NaN output row.
+// Each output value is computed by the same arithmetic wherever its pair sits
+// in a pass, so results are identical run to run.  A pair whose id is outside
+// [0, E) gets a NaN output row.
 #include "block_operand.hpp"
-#include "gemv_mfma.hpp"
 #include "kernels.hpp"
 #include "rows_core.hpp"
 
 namespace mxq {
 
-// ---- grouping ----------------------------------------------------------------------
-
-constexpr int kGroupThreads = 1024;
-
-__global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t* __restrict__ ids, int64_t pairs,
-                                                                  int64_t experts, int32_t* __restrict__ goff,
-                                                                  int32_t* __restrict__ gperm, void* __restrict__ yv,
-                                                                  int y_bf16, int64_t n) {
-    __shared__ int cnt[kMaxGroupExperts];
-    __shared__ int scan[kGroupThreads];
-    const int tid = threadIdx.x;
-    const int E = (int)experts;
-    for (int e = tid; e < E; e += kGroupThreads) cnt[e] = 0;
-    __syncthreads();
-    for (int64_t q = tid; q < pairs; q += kGroupThreads) {
-        const int e = ids[q];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-    }
-    __syncthreads();
-    // inclusive scan of the counts (E <= kGroupThreads) by doubling steps
-    int v = tid < E ? cnt[tid] : 0;
-    scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kGroupThreads; off <<= 1) {
-        const int add = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        v += add;
-        scan[tid] = v;
-        __syncthreads();
-    }
-    if (tid < E) {
-        const int start = v - cnt[tid];
-        goff[tid] = start;
-        cnt[tid] = start;  // running insert position
-    }
-    if (tid == 0) goff[E] = scan[E - 1];
-    __syncthreads();
-    for (int64_t q = tid; q < pairs; q += kGroupThreads) {
-        const int e = ids[q];
-        if (e >= 0 && e < E) {
-            gperm[atomicAdd(&cnt[e], 1)] = (int32_t)q;
-        } else {
-            for (int64_t c = 0; c < n; ++c) {
-                if (y_bf16) reinterpret_cast<uint16_t*>(yv)[q * n + c] = 0x7FC0u;
-                else reinterpret_cast<float*>(yv)[q * n + c] = __builtin_nanf("");
-            }
-        }
-    }
-}
-
-// ---- per-expert matrix-unit product ------------------------------------------------
-
-constexpr int kPairsPerBlock = 16;  // B operand columns
-constexpr int kMoeGemmWaves = 8;    // waves per workgroup (measured on MI355X: 8 beat 4 and 16)
-
-// Grid (row tile, expert).  Wave w owns rows tile*ROWS + (w / KS)*16 .. +15 and
-// k range w % KS; lane (row l % 16, k group g = l / 16) holds MB whole 32-element
-// blocks of its row in registers -- blocks kb0 + 4j + g, j < MB -- loaded once
-// and used for every block of 16 pairs, so the expert's weights leave HBM
-// once per call.
-// XF: the first block's inputs are requested before the weights (below).
-// That keeps their registers live across the weight loads; the 4-bit formats
-// stay within the 128 registers of two workgroups per CU (their LDS allows
-// two) except NVFP4 with eight blocks per lane, which loads its weights first
-// (MI355X, 30B-A3B gate/up bank, 512 tokens: 176 us that way, 223 us with one
-// workgroup per CU).
-template <int FMT, int MB>
-constexpr bool moe_gemm_x_first() { return !(FMT == kNVFP4 && MB == 8); }
-
-template <int FMT, int KS, int MB, bool ROW8>
-__global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
-    const int32_t* __restrict__ goff, const int32_t* __restrict__ gperm, const uint16_t* __restrict__ x,
-    int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
-    static_assert(FMT == kNVFP4, "E2M1 codes with E4M3 block scales (every other row streams)");
-    constexpr int NW = kMoeGemmWaves;
-    constexpr int ROWS = NW / KS * 16;
-    __shared__ __attribute__((aligned(16))) float red[KS > 1 ? NW * 256 : 1];
-    extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];  // [16][k + 8] bf16
-    __shared__ int64_t xrow_of[kPairsPerBlock];                     // input row of each pair of the block
-
-    const int64_t e = blockIdx.y;
-    const int64_t c0 = goff[e];
-    const int64_t cnt = goff[e + 1] - c0;
-    if (cnt <= 0) return;
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int l = tid & 63;
-    const int lr = l & 15;  // row within the wave's 16; also the pair column of the B operand
-    const int g = l >> 4;   // k group
-    const int wr = wave / KS, kp = wave % KS;
-
-    const int64_t rowbytes = code_bytes_per_row(FMT, k);
-    const int64_t sbytes = k / block_elems(FMT);
-    const int64_t nblk = (k + 31) / 32;  // ROW8 (NVFP4, k an odd multiple of 16): the last block is half
-    const int64_t kb0 = (int64_t)kp * MB * 4;
-    const int64_t kb1 = kb0 + MB * 4 < nblk ? kb0 + MB * 4 : nblk;
-    const int64_t rowt = (int64_t)blockIdx.x * ROWS + (int64_t)wr * 16;
-    int64_t row = rowt + lr;
-    row = row < n ? row : n - 1;
-    const uint8_t* crow = codes + (e * n + row) * rowbytes;
-    const uint8_t* srow = scales + (e * n + row) * sbytes;
-    const float gmul = (FMT == kNVFP4) ? gscale[e] : 1.0f;
-
-    // Gather of the input rows of a block of pairs into LDS: piece i of the
-    // block is row i / pieces, 16-byte column i % pieces; a round issues U
-    // pieces per thread (all of a 16 x 2048 block in one round), then stores them.
-    constexpr int U = 8, NT = NW * 64;
-    const int pieces = (int)(k / 8);
-    const int64_t xstride = mfma_x_stride(k);
-    u32x4g_t xv[U];
-    int dst[U];  // LDS 16-byte slot of each piece
-    auto gather_issue = [&](int i0, int total) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * NT < total ? i0 + u * NT : i0;
-            const int bi = i / pieces, ci = i - bi * pieces;
-            dst[u] = bi * (int)(xstride / 8) + ci;
-            xv[u] = *reinterpret_cast<const u32x4g_t*>(x + xrow_of[bi] * k + (int64_t)ci * 8);
-        }
-    };
-    auto gather_store = [&](int i0, int total) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (i0 + u * NT < total) reinterpret_cast<u32x4g_t*>(xlds)[dst[u]] = xv[u];
-    };
-    // The first block's rows are requested before the weights (XF): the loads
-    // complete in order, so storing them to LDS then waits for them alone and
-    // the weights arrive while the workgroup stages and synchronises.
-    constexpr bool XF = moe_gemm_x_first<FMT, MB>();
-    if constexpr (XF) {
-        const int batch = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock);
-        if (tid < batch) xrow_of[tid] = gperm[c0 + tid] / xdiv;
-        __syncthreads();
-        if (tid < batch * pieces) gather_issue(tid, batch * pieces);
-    }
-
-    // the lane's weight blocks: loaded once; blocks outside the k range read
-    // a valid block and are zeroed (codes 0, unit scale)
-    WFrag<FMT> w[MB];
-    uint32_t valid = 0;
-#pragma unroll
-    for (int j = 0; j < MB; ++j) {
-        const int64_t b = kb0 + 4 * j + g;
-        const bool ok = b < kb1;
-        valid |= (ok ? 1u : 0u) << j;
-        if constexpr (ROW8) load_wfrag<FMT, 32, true>(crow, srow, (ok ? b : 0) * 32, k, w[j]);
-        else load_block<FMT>(crow, srow, ok ? b : 0, w[j]);
-    }
-
-    // the rest of the first block's staging
-    if constexpr (XF) {
-        const int total = (int)(cnt < kPairsPerBlock ? cnt : kPairsPerBlock) * pieces;
-        if (tid < total) gather_store(tid, total);
-        for (int i0 = tid + U * NT; i0 < total; i0 += U * NT) {
-            gather_issue(i0, total);
-            gather_store(i0, total);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < MB; ++j) {
-        const bool ok = (valid >> j) & 1u;
-#pragma unroll
-        for (int d = 0; d < WFrag<FMT>::DW; ++d) w[j].w[d] = ok ? w[j].w[d] : 0u;
-        w[j].s = ok ? w[j].s : (FMT == kNVFP4 ? 0x3838u : 127u);
-    }
-
-    for (int64_t t0 = 0; t0 < cnt; t0 += kPairsPerBlock) {
-        const int batch = (int)(cnt - t0 < kPairsPerBlock ? cnt - t0 : kPairsPerBlock);
-        const bool xlive = lr < batch;
-        if (t0 > 0 || !XF) {
-            const int total = batch * pieces;
-            __syncthreads();  // the previous block's LDS reads are done
-            if (tid < batch) xrow_of[tid] = gperm[c0 + t0 + tid] / xdiv;
-            __syncthreads();
-            for (int i0 = tid; i0 < total; i0 += U * NT) {
-                gather_issue(i0, total);
-                gather_store(i0, total);
-            }
-        }
-        __syncthreads();
-
-        f32x4m_t acc = {0.f, 0.f, 0.f, 0.f};
-        const u32x4g_t* xp0 = reinterpret_cast<const u32x4g_t*>(xlds) + ((int64_t)lr * xstride + (kb0 + g) * 32) / 8;
-        // B operands of block j (4 x 16 bytes of the pair's input), zero for
-        // pairs past the block and blocks outside the k range
-        auto read_x = [&](int j, u32x4g_t(&v)[4]) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) v[s4] = u32x4g_t{0u, 0u, 0u, 0u};
-            if (xlive && ((valid >> j) & 1u)) {
-                // ROW8: the last block is half; its staged row ends at k (no read past it)
-                const bool half = ROW8 && (kb0 + 4 * j + g) * 32 + 32 > k;
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    if (!(half && s4 >= 2)) v[s4] = xp0[j * 16 + s4];
-            }
-        };
-        u32x4g_t vb[2][4];
-        read_x(0, vb[0]);
-#pragma unroll
-        for (int j = 0; j < MB; ++j) {
-            // the reads of block j + 1 are issued before the MFMAs of block j;
-            // the empty asm keeps the compiler from hoisting later reads
-            // (which would hold every block's operands in registers at once)
-            if (j + 1 < MB) read_x(j + 1, vb[(j + 1) & 1]);
-            const u32x4g_t(&v)[4] = vb[j & 1];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 0>(w[j]), __builtin_bit_cast(bf16x8_t, v[0]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 1>(w[j]), __builtin_bit_cast(bf16x8_t, v[1]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 2>(w[j]), __builtin_bit_cast(bf16x8_t, v[2]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(decode_step<FMT, 3>(w[j]), __builtin_bit_cast(bf16x8_t, v[3]), acc, 0, 0, 0);
-            asm volatile("" ::: "memory");
-        }
-
-        // k-split sums in a fixed order, then the block's outputs
-        if constexpr (KS > 1) {
-            *reinterpret_cast<f32x4m_t*>(red + (wave * 64 + l) * 4) = acc;
-            __syncthreads();
-            if (kp == 0) {
-#pragma unroll
-                for (int q = 1; q < KS; ++q) acc += *reinterpret_cast<const f32x4m_t*>(red + ((wave + q) * 64 + l) * 4);
-            }
-        }
-        if (kp == 0 && xlive) {
-            const int64_t q = gperm[c0 + t0 + lr];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int64_t r = rowt + 4 * g + ii;
-                if (r < n) {
-                    const float v = acc[ii] * gmul;
-                    if (y_bf16) reinterpret_cast<uint16_t*>(yv)[q * n + r] = f32_to_bf16_rne(v);
-                    else reinterpret_cast<float*>(yv)[q * n + r] = v;
-                }
-            }
-        }
-    }
-}
-
-// ---- streaming variant (E2M1 codes, whole 32-element blocks) -------------------------
+// ---- the streaming kernel -----------------------------------------------------------
 //
 // Grid (tile of 256 weight rows, expert).  Wave w owns weight rows tile*256 +
 // 32w .. +31, one 32-row block of 32x32x16 bf16 MFMAs (the B operand's
@@ -283,9 +30,11 @@ __global__ __launch_bounds__(kMoeGemmWaves * 64) __attribute__((amdgpu_waves_per
 // decoded to bf16 in registers; lane (l32, h) holds the 16 bytes of codes of
 // half h of the slice of its row l32 (the k order of gemm.hip).  Codes and gathered inputs stream through
 // rings of slices in registers, each slot refilled as soon as it is used, so
-// a wave keeps loads in flight from start to end, as the GEMV engine does; the register-resident kernel above instead
-// loads its whole tile first and then computes, and two such workgroups per
-// CU leave HBM idle while both compute.
+// a wave keeps loads in flight from start to end, as the GEMV engine does (a
+// kernel that first loaded its whole tile into registers and then computed
+// left HBM idle while its two workgroups per CU computed).  NVFP4 rows of an
+// odd number of 16-element blocks (ROW8: 8-byte aligned rows) load each
+// 16-byte share as two 8-byte halves; the row's last share holds one block.
 typedef float f32x16m_t __attribute__((ext_vector_type(16)));
 // Slices in flight: kMgDepthW of codes per lane, kMgDepthX of gathered inputs
 // per thread (kMgDepthW divides kMgDepthX, the loop's unroll).  MI355X,
@@ -305,11 +54,12 @@ struct MgSlice {
     static constexpr int EPT = BK / 8;    // gathered input elements per thread and slice (64 pairs, 512 threads)
 };
 
-template <int FMT>
+template <int FMT, bool ROW8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void moe_gemm_stream_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, const float* __restrict__ gscale,
     const int32_t* __restrict__ ids, int64_t pairs, int64_t experts, const uint16_t* __restrict__ x,
     int64_t xdiv, void* __restrict__ yv, int y_bf16, int64_t n, int64_t k) {
+    static_assert(!ROW8 || FMT == kNVFP4, "only NVFP4 rows can be 8-byte multiples");
     using MS = MgSlice<FMT>;
     constexpr int kMgBK = MS::BK, kMgXStride = MS::XS, KE = MS::KE, EPT = MS::EPT;
     using XPiece = std::conditional_t<EPT == 8, u32x4g_t, u32x2g_t>;
@@ -357,18 +107,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     auto load_w = [&](int64_t s, Frag& f) {
         const int64_t kb = s * kMgBK + half * KE;
         const int64_t kc = kb < k ? kb : 0;
-        const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + (FMT == kMXFP8 ? kc : kc / 2));
+        if constexpr (ROW8) {
+            // two 8-byte halves; a share whose second block lies past the row end
+            // reads its first half twice and its first scale twice (selected away
+            // where the share is decoded)
+            const int64_t hi = kc + 32 <= k ? 8 : 0;
+            const u32x2g_t v0 = *reinterpret_cast<const u32x2g_t*>(crow + kc / 2);
+            const u32x2g_t v1 = *reinterpret_cast<const u32x2g_t*>(crow + kc / 2 + hi);
+            f.w[0] = v0[0];
+            f.w[1] = v0[1];
+            f.w[2] = v1[0];
+            f.w[3] = v1[1];
+            f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + hi / 8] << 8);
+        } else {
+            const u32x4g_t v = *reinterpret_cast<const u32x4g_t*>(crow + (FMT == kMXFP8 ? kc : kc / 2));
 #pragma unroll
-        for (int d = 0; d < 4; ++d) f.w[d] = v[d];
-        if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
-        else f.s = srow[kc / 32];
+            for (int d = 0; d < 4; ++d) f.w[d] = v[d];
+            if constexpr (FMT == kNVFP4) f.s = (uint32_t)srow[kc / 16] | ((uint32_t)srow[kc / 16 + 1] << 8);
+            else f.s = srow[kc / 32];
+        }
     };
     auto live = [&](int64_t s, const Frag& f) {
-        const bool ok = s * kMgBK + half * KE < k;
+        const int64_t kb = s * kMgBK + half * KE;
+        const bool ok = kb < k;
+        const bool ok2 = ROW8 ? kb + 32 <= k : ok;  // the share's second 16-element block
         Frag g;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) g.w[d] = ok ? f.w[d] : 0u;
-        g.s = ok ? f.s : (FMT == kNVFP4 ? 0x3838u : 127u);
+        g.w[0] = ok ? f.w[0] : 0u;
+        g.w[1] = ok ? f.w[1] : 0u;
+        g.w[2] = ok2 ? f.w[2] : 0u;
+        g.w[3] = ok2 ? f.w[3] : 0u;
+        if constexpr (FMT == kNVFP4) g.s = (ok ? (f.s & 0xFFu) : 0x38u) | (ok2 ? (f.s & 0xFF00u) : 0x3800u);
+        else g.s = ok ? f.s : 127u;
         return g;
     };
     for (;;) {
@@ -551,75 +320,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
     }
 }
 
-template <int FMT>
+template <int FMT, bool ROW8>
 static void launch_moe_gemm_stream(const MoeGemmArgs& a, hipStream_t st) {
     const int64_t tiles = (a.n + kMgRows - 1) / kMgRows;
-    hipLaunchKernelGGL(moe_gemm_stream_kernel<FMT>, dim3((unsigned)tiles, (unsigned)a.experts), dim3(512), 0, st,
-                       a.codes, a.scales, a.gscale, a.ids, a.m * a.topk, a.experts, a.x,
+    hipLaunchKernelGGL((moe_gemm_stream_kernel<FMT, ROW8>), dim3((unsigned)tiles, (unsigned)a.experts), dim3(512), 0,
+                       st, a.codes, a.scales, a.gscale, a.ids, a.m * a.topk, a.experts, a.x,
                        a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
-}
-
-// The register-resident kernel runs NVFP4 rows of an odd number of 16-element
-// blocks (8-byte rows); everything else takes the streaming kernel.
-template <int FMT, int KS, int MB>
-static void launch_moe_gemm_ks(const MoeGemmArgs& a, const int32_t* goff, const int32_t* gperm, hipStream_t st) {
-    constexpr int ROWS = kMoeGemmWaves / KS * 16;
-    const int64_t tiles = (a.n + ROWS - 1) / ROWS;
-    static_assert(kPairsPerBlock == 16, "moe_gemm_x_lds assumes blocks of 16 pairs");
-    hipLaunchKernelGGL((moe_gemm_kernel<FMT, KS, MB, FMT == kNVFP4>), dim3((unsigned)tiles, (unsigned)a.experts),
-                       dim3(kMoeGemmWaves * 64), (size_t)moe_gemm_x_lds(a.k), st, a.codes, a.scales, a.gscale, goff,
-                       gperm, a.x, a.x_per_slot ? (int64_t)1 : a.topk, a.y, a.y_bf16, a.n, a.k);
-}
-
-// Streaming kernel: rows of whole 32-element blocks (every MX row; NVFP4 with
-// k % 32 == 0).  Register-resident kernel (the other NVFP4 rows), register
-// blocks per lane (MB) and k split (KS): the smallest capacity 4 * MB * KS
-// blocks that holds the row, at most 8 blocks per lane (MI355X, 30B-A3B gate/up
-// bank in MXFP4, 512-token prompt: 2 x 8 148 us, 1 x 16 162 us, 4 x 4 179 us;
-// its down bank: 1 x 6 93 us, 2 x 4 129 us).
-template <int FMT>
-static bool launch_moe_gemm_inst(const MoeGemmArgs& a, hipStream_t st) {
-    const int64_t pairs = a.m * a.topk;
-    int32_t* goff = a.workspace;
-    int32_t* gperm = a.workspace + a.experts + 1;
-    auto group = [&]() {
-        hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, st, a.ids, pairs, a.experts, goff,
-                           gperm, a.y, a.y_bf16, a.n);
-    };
-    if (a.k % 32 == 0) {
-        launch_moe_gemm_stream<FMT>(a, st);
-        return true;
-    }
-    if constexpr (FMT != kNVFP4) {
-        return false;  // MX rows are whole 32-element blocks
-    } else {
-        const int64_t nblk = (a.k + 31) / 32;
-        static constexpr int kCand4[][2] = {{1, 4}, {1, 6}, {1, 8}, {2, 6}, {2, 8}, {4, 6}, {4, 8}};
-        int best_ks = 0, best_mb = 0;
-        int64_t best_cap = 0;
-        auto consider = [&](int ks, int mb) {
-            const int64_t cap = 4LL * ks * mb;
-            if (cap >= nblk && (best_ks == 0 || cap < best_cap)) { best_ks = ks; best_mb = mb; best_cap = cap; }
-        };
-        for (const auto& c : kCand4) consider(c[0], c[1]);
-        if (best_ks == 0) return false;
-        group();
-#define MXQ_MG_CASE(KS_, MB_) \
-    if (best_ks == KS_ && best_mb == MB_) { launch_moe_gemm_ks<FMT, KS_, MB_>(a, goff, gperm, st); return true; }
-        MXQ_MG_CASE(1, 4) MXQ_MG_CASE(1, 6) MXQ_MG_CASE(1, 8) MXQ_MG_CASE(2, 6) MXQ_MG_CASE(2, 8) MXQ_MG_CASE(4, 6)
-        MXQ_MG_CASE(4, 8)
-#undef MXQ_MG_CASE
-        return false;
-    }
 }
 
 bool launch_moe_gemm(const MoeGemmArgs& a, hipStream_t st) {
     if (a.experts > kMaxGroupExperts) return false;
-    if (a.k % 32 != 0 && moe_gemm_x_lds(a.k) > kMoeGemmMaxXLds) return false;  // (the staging kernel's LDS)
     switch (a.fmt) {
-        case kMXFP4: return launch_moe_gemm_inst<kMXFP4>(a, st);
-        case kMXFP8: return launch_moe_gemm_inst<kMXFP8>(a, st);
-        case kNVFP4: return launch_moe_gemm_inst<kNVFP4>(a, st);
+        case kMXFP4:
+            if (a.k % 32 != 0) return false;  // MX rows are whole 32-element blocks
+            launch_moe_gemm_stream<kMXFP4, false>(a, st);
+            return true;
+        case kMXFP8:
+            if (a.k % 32 != 0) return false;
+            launch_moe_gemm_stream<kMXFP8, false>(a, st);
+            return true;
+        case kNVFP4:
+            if (a.k % 32 == 0) launch_moe_gemm_stream<kNVFP4, false>(a, st);
+            else launch_moe_gemm_stream<kNVFP4, true>(a, st);
+            return true;
     }
     return false;
 }

@@ -299,11 +299,9 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  * processes the tokens expert by expert for its MXFP4 MoE prefill gain; here
  * the routed (token, slot) pairs are grouped by expert on the GPU and each
  * expert's weights are decoded to bf16 and multiplied on the matrix unit with
- * its pairs' inputs (fp32 accumulate): for rows of whole 32-element blocks
- * (MXFP4, MXFP8, NVFP4 with k % 32 == 0) one kernel streams each expert's rows
- * against 64 of its pairs at a time, finding them in the ids itself; NVFP4
- * rows of an odd number of 16-element blocks are grouped by a first kernel
- * into the workspace, then multiplied 16 pairs at a time:
+ * its pairs' inputs (fp32 accumulate): one kernel streams each expert's rows
+ * against 64 of its pairs at a time, finding them in the ids itself, in every
+ * format and at every k:
  *
  *   y[t][s][i] = sum_k W[expert_ids[t][s]][i][k] * x_ts[k]
  *   x_ts = x[t] (x_per_slot == 0, e.g. gate/up) or x[t][s] (x_per_slot != 0, e.g. down)
@@ -313,17 +311,13 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  *   expert_ids     int32 [m][topk]; x bf16 [m][k] or [m][topk][k]
  *   y              [m][topk][n], bf16 (RNE of the fp32 value) or fp32 (y_dtype)
  *   workspace      int32 [num_experts + 1 + m * topk], caller-owned, 4-byte
- *                  aligned: per-expert offsets, then the grouped pair order
- *                  (written by the grouping kernel where it runs; otherwise
- *                  left as it was)
+ *                  aligned scratch; the current kernel neither reads nor
+ *                  writes it
  *   m 1 .. 2^24 / topk;  topk 1 .. MXQ_MAX_TOPK;  num_experts 1 .. 1024;
  *   n >= 1;  k a positive multiple of the block size (32 MX, 16 NVFP4), up
- *   to 2^31 - 1; NVFP4 rows of an odd number of 16-element blocks at most 4088
- *   (the inputs of 16 pairs are staged in 128 KiB of LDS; larger k gives
- *   MXQ_E_UNSUPPORTED)
+ *   to 2^31 - 1
  * A pair whose id is outside [0, num_experts) gets a NaN output row.  The
- * kernels run on `stream`; the workspace must not be shared by calls that
- * overlap.
+ * kernel runs on `stream`.
  */
 mxq_status_t mxq_moe_gemm(mxq_format_t fmt, const uint8_t *codes, const uint8_t *scales, const float *global_scale,
                           const int32_t *expert_ids, const uint16_t *x, int x_per_slot, void *y, mxq_out_t y_dtype,

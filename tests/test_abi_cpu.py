@@ -194,10 +194,9 @@ def test_unsupported_sizes():
     assert block_rt(T=9) == UNSUPPORTED and block_rt(E=1025) == UNSUPPORTED and block_rt(topk=8, dff=4128) == UNSUPPORTED
     assert mgemm(topk=17) == UNSUPPORTED and mgemm(E=1025) == UNSUPPORTED
     assert mgemm(m=(1 << 24) // 8 + 1, topk=8) == UNSUPPORTED and mgemm(n=1 << 31) == UNSUPPORTED
-    # only NVFP4 rows of an odd number of 16-element blocks stage 16 padded input rows in
-    # 128 KiB of LDS; other rows stream at any k
-    assert mgemm(fmt=3, g=A, k=4112) == UNSUPPORTED and mgemm(fmt=3, g=A, k=4080) == DEVICE
-    assert mgemm(k=4096) == DEVICE and mgemm(fmt=3, g=A, k=8192) == DEVICE and mgemm(fmt=2, k=65536) == DEVICE
+    # every row streams, at any k (no staging of whole input rows)
+    assert mgemm(fmt=3, g=A, k=4112) == DEVICE and mgemm(fmt=3, g=A, k=4080) == DEVICE
+    assert mgemm(k=4096) == DEVICE and mgemm(fmt=3, g=A, k=8208) == DEVICE and mgemm(fmt=2, k=65536) == DEVICE
     assert quant(rows=1 << 20, k=(1 << 16) + 32) == UNSUPPORTED and quant(rows=1 << 31) == UNSUPPORTED
 
 

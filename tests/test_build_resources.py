@@ -21,7 +21,7 @@ def _usage():
 def test_every_kernel_recorded():
     usage = _usage()
     assert len(usage) > 100, f"only {len(usage)} kernels recorded"
-    for name in ("gemm_kernel", "moe_gemm_kernel", "gemv_rows_kernel", "gemv_mfma_kernel", "moe_kernel",
+    for name in ("gemm_kernel", "moe_gemm_stream_kernel", "gemv_rows_kernel", "gemv_mfma_kernel", "moe_kernel",
                  "moe_down_kernel", "moe_route_kernel", "quantize_kernel", "requant_fp8_kernel", "dequant_kernel"):
         assert any(name in k for k in usage), f"{name} missing from the build record"
 

@@ -181,12 +181,11 @@ def test_streaming_kernel_across_k(fmt, k):
     check(c, f"moe gemm streaming {FMT_NAMES[fmt]} k={k}")
 
 
-@pytest.mark.parametrize("k", [16, 48, 496, 752, 1008, 1520, 2032, 3056, 4080])
-def test_register_tile_variants(k):
-    """NVFP4 rows of an odd number of 16-element blocks take the per-expert
-    register-resident kernel; these lengths select every (k split, register
-    blocks per lane) variant -- 1 x 4 (up to 16 blocks of 32), 1 x 6 (24),
-    1 x 8 (32), 2 x 6 (48), 2 x 8 (64), 4 x 6 (96), 4 x 8 (128) -- each with
-    the row's last block half; every output checked."""
+@pytest.mark.parametrize("k", [16, 48, 80, 496, 752, 1008, 2032, 4080, 4112, 8208])
+def test_nvfp4_8_byte_rows_across_k(k):
+    """NVFP4 rows of an odd number of 16-element blocks (8-byte aligned rows):
+    the streaming kernel loads each lane's share as two 8-byte halves and the
+    row's last share holds one block; one slice or many, the last share in
+    either half of its slice, rows past 4088; every output checked."""
     c = case(3, 8, 40, k, 21, 3, 170 + k)
-    check(c, f"moe gemm register variants nvfp4 k={k}")
+    check(c, f"moe gemm nvfp4 8-byte rows k={k}")
