@@ -297,10 +297,10 @@ mxq_status_t mxq_moe_block_noalloc(mxq_format_t fmt, const uint8_t *gu_codes, co
  * Expert-batched MoE GEMM (prefill).  The "Decoding block-float formats in
  * software" section of the "MLxcel 0.8 release" post credits a kernel that
  * processes the tokens expert by expert for its MXFP4 MoE prefill gain; here
- * the routed (token, slot) pairs are grouped by expert on the GPU and each
- * expert's weights are decoded to bf16 and multiplied on the matrix unit with
- * its pairs' inputs (fp32 accumulate): one kernel streams each expert's rows
- * against 64 of its pairs at a time, finding them in the ids itself, in every
+ * each expert's weights are decoded to bf16 and multiplied on the matrix unit
+ * with the inputs of the (token, slot) pairs routed to it (fp32 accumulate):
+ * one kernel streams each expert's rows against 64 of its pairs at a time,
+ * finding them in the ids itself (no host sync, no grouping pass), in every
  * format and at every k:
  *
  *   y[t][s][i] = sum_k W[expert_ids[t][s]][i][k] * x_ts[k]
