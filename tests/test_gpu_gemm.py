@@ -64,12 +64,13 @@ def test_nvfp4_rows_of_an_odd_number_of_blocks(m, n, k):
     assert torch.equal(y16.cpu().view(torch.int16), y32.cpu().to(torch.bfloat16).view(torch.int16))
 
 
-@pytest.mark.parametrize("fmt", [1, 2, 3])
-def test_last_round_in_smaller_tiles(fmt):
+@pytest.mark.parametrize("fmt,k", [(1, 64), (2, 64), (3, 64), (3, 80)])
+def test_last_round_in_smaller_tiles(fmt, k):
     """260 x 33357: 2 x 131 tiles of 256 x 256 leave a partly filled last round on
     a 256-CU device (one workgroup per CU), so the last 3 tile columns (589
-    columns, ragged) run as a second launch of 128 x 128 tiles; every output."""
-    m, n, k = 260, 33357, 64
+    columns, ragged) run as a second launch of 128 x 128 tiles; NVFP4 also with
+    8-byte rows (k = 80); every output."""
+    m, n = 260, 33357
     c = small_case(fmt, m, n, k, 400 + fmt)
     say("gemm last round in smaller tiles", fmt)
     Y = host(mxq.gemm(fmt, dev_u8(c["codes"]), dev_u8(c["scales"]), dev_bf16(c["x"]), dev_f32(c["g"]),
